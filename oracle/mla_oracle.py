@@ -1,0 +1,269 @@
+"""Plain float64 NumPy oracle for DeepSeek-V2 Multi-head Latent Attention (MLA).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.  Slow on purpose: no
+blocking, no fusion, no reordering beyond what each definition states; library
+matrix products serve as single steps.
+
+Sources (page title, section / equation):
+  * "A. Conclusion, Limitation, and Future" DeepSeek-V2 reading notes
+    (irregular6612.github.io), §2.1.1 eq. 1-8 (standard MHA, per-head split,
+    scaled-dot softmax attention) and §2.1.2 eq. 9-13 (low-rank joint KV
+    compression, up-projections W^UK / W^UV, query compression).
+  * DeepSeek-V2 MLA blog (adg.csdn.net), part 2 §2.2.1.1 (only c^KV is cached;
+    W^UK / W^UV can be absorbed), §2.2.2 (RoPE as position rotation matrices
+    with R_m^T R_n depending on n - m; RoPE is incompatible with the low-rank
+    cache; decoupled multi-head q^R and one shared k^R; concatenation
+    [q^C; q^R], [k^C; k^R]; k^R is cached already rotated; cache holds
+    (d_c + d_R) elements per token, d_c = 4 d_h, d_R = d_h / 2).
+
+Readings where the pages are silent or garbled (every one is also listed in the
+design notes):
+  R1 softmax scale: 1/sqrt(d_h + d_R), the width of the concatenated q.k.
+  R2 RoPE: rotate adjacent pairs (x[2k], x[2k+1]) by pos * base^(-2k/d_R),
+     angles formed in float64.
+  R3 k^R is stored after rotation at its own position; c^KV is never rotated.
+  R4 cached token j sits at position j; a decode query sits at position L and
+     sees all L cached keys; chunk row m of a q_len-row chunk sees keys
+     j < L - (q_len - 1 - m) (its own position included).
+  R5 eq. 7's printed sum index is read as a sum over keys j.
+  R6 a query row with no visible key yields o = 0 and lse = -inf.
+  R7 W^UK / W^UV are stored [n_h, d_h, d_c]: head i owns rows i*d_h..(i+1)*d_h
+     of eq. 10/11's matrices (eq. 4-6 ordering).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rope_rotate", "mla_attention_naive", "kv_cache_rows", "absorb_query",
+    "latent_attention", "split_ranges", "combine_splits", "out_projection",
+    "visible_keys", "mla_reference_problem",
+]
+
+F64 = np.float64
+
+
+def rope_rotate(x, pos, base: float):
+    """Apply the position rotation R_pos to the trailing axis of ``x``.
+
+    blog §2.2.2: RoPE multiplies a vector by a position-dependent rotation
+    matrix so that (R_m q)^T (R_n k) depends on n - m only.  Reading R2: the
+    matrix is block diagonal with 2x2 rotations on adjacent pairs, pair k
+    turned by angle pos * base^(-2k/d), d = x.shape[-1].
+
+    ``pos`` broadcasts against ``x.shape[:-1]``.
+    """
+    x = np.asarray(x, dtype=F64)
+    d = x.shape[-1]
+    if d % 2:
+        raise ValueError("RoPE width must be even")
+    if d == 0:
+        return x.copy()
+    k = np.arange(d // 2, dtype=F64)
+    theta = float(base) ** (-2.0 * k / d)
+    ang = np.asarray(pos, dtype=F64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    even, odd = x[..., 0::2], x[..., 1::2]
+    out = np.empty(np.broadcast_shapes(x.shape, ang.shape[:-1] + (d,)), dtype=F64)
+    out[..., 0::2] = even * c - odd * s
+    out[..., 1::2] = even * s + odd * c
+    return out
+
+
+def visible_keys(seq_len: int, q_len: int) -> np.ndarray:
+    """Keys visible to each of the q_len query rows of one sequence (reading R4)."""
+    return np.array([seq_len - (q_len - 1 - m) for m in range(q_len)], dtype=np.int64)
+
+
+def _softmax_two_pass(s):
+    """eq. 7's Softmax_j over the last axis, two passes (max, then normalised exp).
+
+    Returns (p, lse).  An empty axis gives an empty p and lse = -inf (R6).
+    """
+    if s.shape[-1] == 0:
+        return s.copy(), np.full(s.shape[:-1], -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=-1, keepdims=True)
+    return e / z, (m + np.log(z))[..., 0]
+
+
+def mla_attention_naive(c_kv, k_r, q_nope, q_rope, w_uk, w_uv, key_pos, q_pos,
+                        n_visible, scale: float, base: float):
+    """MLA attention of one sequence in the literal, non-absorbed form.
+
+    Inputs (any float type, used as float64):
+      c_kv [L, d_c]   cached latents c^KV_j (eq. 9's output; given)
+      k_r  [L, d_R]   decoupled RoPE key before rotation, shared by all heads
+      q_nope [M, n_h, d_h], q_rope [M, n_h, d_R]  the M query rows
+      w_uk, w_uv [n_h, d_h, d_c]
+      key_pos [L], q_pos [M], n_visible [M] (row m sees keys 0..n_visible[m]-1)
+    Steps, per head i:
+      k^C_{j,i} = W^UK_i c^KV_j and v^C_{j,i} = W^UV_i c^KV_j  (eq. 10, 11)
+      k^R_j = R_{pos j} k_r_j, q^R_i = R_{q pos} q_rope_i       (blog §2.2.2)
+      q_i = [q_nope_i; q^R_i], k_{j,i} = [k^C_{j,i}; k^R_j]      (blog §2.2.2)
+      o_i = sum_j Softmax_j(scale * q_i . k_{j,i}) v^C_{j,i}     (eq. 7)
+    Returns out [M, n_h, d_h] (eq. 7's o_{t,i}, before W^O), lse [M, n_h] and
+    the diagnostic o_lat [M, n_h, d_c] = sum_j p_j c^KV_j.
+    """
+    c_kv = np.asarray(c_kv, F64)
+    k_r = np.asarray(k_r, F64)
+    q_nope = np.asarray(q_nope, F64)
+    q_rope = np.asarray(q_rope, F64)
+    w_uk = np.asarray(w_uk, F64)
+    w_uv = np.asarray(w_uv, F64)
+    M, n_h, d_h = q_nope.shape
+    d_c = c_kv.shape[1]
+    k_rot = rope_rotate(k_r, np.asarray(key_pos), base)                  # [L, d_R]
+    q_rot = rope_rotate(q_rope, np.asarray(q_pos)[:, None], base)        # [M, n_h, d_R]
+    out = np.zeros((M, n_h, d_h))
+    o_lat = np.zeros((M, n_h, d_c))
+    lse = np.full((M, n_h), -np.inf)
+    n_visible = np.asarray(n_visible, dtype=np.int64)
+    for i in range(n_h):
+        k_c = c_kv @ w_uk[i].T          # [L, d_h]   eq. 10 for every cached token
+        v_c = c_kv @ w_uv[i].T          # [L, d_h]   eq. 11
+        keys = np.concatenate([k_c, k_rot], axis=1)   # [L, d_h + d_R]
+        for m in range(M):
+            n = int(n_visible[m])
+            if n <= 0:
+                continue
+            q = np.concatenate([q_nope[m, i], q_rot[m, i]])
+            s = (keys[:n] @ q) * scale
+            p, l = _softmax_two_pass(s)
+            out[m, i] = p @ v_c[:n]
+            o_lat[m, i] = p @ c_kv[:n]
+            lse[m, i] = l
+    return out, lse, o_lat
+
+
+# ---------------------------------------------------------------------------
+# The absorbed steps, each with its plain definition.  Together they equal
+# mla_attention_naive by associativity (blog §2.2.1.1 / §2.2.2: W^UK moves to
+# the query side and W^UV to the output side).
+# ---------------------------------------------------------------------------
+
+def kv_cache_rows(c_kv, k_r, pos, base: float):
+    """The cached row of each token: [c^KV_j ; R_{pos j} k_r_j] (readings R3, R4).
+
+    blog §2.2.2: per token the cache keeps c^KV and the already rotated k^R,
+    (d_c + d_R) elements.  Returns float64 [N, d_c + d_R].
+    """
+    c_kv = np.asarray(c_kv, F64)
+    return np.concatenate([c_kv, rope_rotate(k_r, np.asarray(pos), base)], axis=1)
+
+
+def absorb_query(q_nope, q_rope, w_uk, q_pos, base: float):
+    """Latent-space query of every row and head: [W^UK_i^T q_nope_i ; R_p q_rope_i].
+
+    By eq. 10, q_nope_i . k^C_{j,i} = q_nope_i . (W^UK_i c_j) = (W^UK_i^T q_nope_i) . c_j,
+    so scoring the absorbed query against the cached latent equals the
+    non-absorbed score.  Returns float64 [T, n_h, d_c + d_R].
+    """
+    q_nope = np.asarray(q_nope, F64)
+    w_uk = np.asarray(w_uk, F64)
+    T, n_h, _ = q_nope.shape
+    q_abs = np.empty((T, n_h, w_uk.shape[2]))
+    for i in range(n_h):
+        q_abs[:, i, :] = q_nope[:, i, :] @ w_uk[i]      # row-vector form of W^T q
+    q_rot = rope_rotate(q_rope, np.asarray(q_pos)[:, None], base)
+    return np.concatenate([q_abs, q_rot], axis=2)
+
+
+def latent_attention(q_lat, rows, n_visible, scale: float, d_c: int):
+    """Attention of latent queries over cached rows (the absorbed eq. 7).
+
+    q_lat [M, n_h, W] with W = d_c + d_R, rows [L, W].  Row m sees rows
+    0..n_visible[m]-1.  s = scale * q_lat . row; p = Softmax_j(s);
+    o_lat = sum_j p_j row_j[:d_c].  Returns (o_lat [M, n_h, d_c], lse [M, n_h]).
+    """
+    q_lat = np.asarray(q_lat, F64)
+    rows = np.asarray(rows, F64)
+    M, n_h, _ = q_lat.shape
+    o_lat = np.zeros((M, n_h, d_c))
+    lse = np.full((M, n_h), -np.inf)
+    for m in range(M):
+        n = int(n_visible[m])
+        if n <= 0:
+            continue
+        s = (q_lat[m] @ rows[:n].T) * scale                 # [n_h, n]
+        p, l = _softmax_two_pass(s)
+        o_lat[m] = p @ rows[:n, :d_c]
+        lse[m] = l
+    return o_lat, lse
+
+
+def split_ranges(n_keys: int, block_size: int, num_splits: int):
+    """Key ranges of the split-KV partition of one sequence.
+
+    The sequence's blocks are cut into num_splits contiguous runs of
+    c = ceil(nblk / num_splits) blocks (the last runs may be short or empty);
+    split s covers keys [s*c*bs, min((s+1)*c*bs, n_keys)).  Empty splits are
+    returned as (e, e) with e = min(s*c*bs, n_keys).
+    """
+    if num_splits < 1 or block_size < 1 or n_keys < 0:
+        raise ValueError("bad split arguments")
+    nblk = -(-n_keys // block_size)
+    c = -(-nblk // num_splits) if nblk else 0
+    out = []
+    for s in range(num_splits):
+        lo = min(s * c * block_size, n_keys)
+        hi = min((s + 1) * c * block_size, n_keys)
+        out.append((lo, hi))
+    return out
+
+
+def combine_splits(o_parts, lse_parts):
+    """Merge softmax partials of disjoint key sets.
+
+    With lse_s = log sum_{j in s} exp(s_j) and o_s = the normalised output of
+    split s, the full softmax output is sum_s exp(lse_s - LSE) o_s with
+    LSE = log sum_s exp(lse_s): an exact identity of softmax over a partition.
+    Splits with lse = -inf (no keys) get weight 0; all-empty gives o = 0,
+    LSE = -inf.  o_parts [S, ..., d], lse_parts [S, ...].
+    """
+    o_parts = np.asarray(o_parts, F64)
+    lse_parts = np.asarray(lse_parts, F64)
+    mx = lse_parts.max(axis=0)
+    finite = np.isfinite(mx)
+    safe = np.where(finite, mx, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - safe), 0.0)
+    z = w.sum(axis=0)
+    lse = np.where(finite, safe + np.log(np.where(finite, z, 1.0)), -np.inf)
+    zz = np.where(finite, z, 1.0)
+    o = (w[..., None] * o_parts).sum(axis=0) / zz[..., None]
+    o = np.where(finite[..., None], o, 0.0)
+    return o, lse
+
+
+def out_projection(o_lat, w_uv):
+    """o_i = W^UV_i o_lat_i for every row and head (eq. 11 moved past the softmax sum).
+
+    o_lat [T, n_h, d_c], w_uv [n_h, d_h, d_c] -> [T, n_h, d_h].
+    """
+    o_lat = np.asarray(o_lat, F64)
+    w_uv = np.asarray(w_uv, F64)
+    T, n_h, _ = o_lat.shape
+    out = np.empty((T, n_h, w_uv.shape[1]))
+    for i in range(n_h):
+        out[:, i, :] = o_lat[:, i, :] @ w_uv[i].T
+    return out
+
+
+def mla_reference_problem(seq_c_kv, seq_k_r, q_nope, q_rope, w_uk, w_uv, seq_len: int,
+                          q_len: int, q_pos, scale: float, base: float, heads=None):
+    """Non-absorbed reference of one sequence's q_len query rows.
+
+    Keys sit at positions 0..seq_len-1 (R4).  ``heads`` optionally restricts
+    the evaluation to a subset of heads (for sampled checks at full size).
+    Returns (out, lse, o_lat) for the selected heads.
+    """
+    L = int(seq_len)
+    if heads is not None:
+        heads = np.asarray(heads)
+        q_nope, q_rope = q_nope[:, heads], q_rope[:, heads]
+        w_uk, w_uv = w_uk[heads], w_uv[heads]
+    return mla_attention_naive(seq_c_kv[:L], seq_k_r[:L], q_nope, q_rope, w_uk, w_uv,
+                               np.arange(L), np.asarray(q_pos), visible_keys(L, q_len),
+                               scale, base)

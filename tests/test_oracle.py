@@ -1,0 +1,314 @@
+"""Pins of the float64 CPU oracle against facts it does not itself compute.
+
+Every test here runs on the CPU.  Each pin targets a plausible mistake in the
+oracle: a dropped term (brute force, L = 1, q = 0), a wrong sign or pairing in
+RoPE (complex-number form, relative-position property), a transposed weight
+(non-square tiny shapes, absorbed == non-absorbed), a wrong scale or softmax
+(library attention, rows summing to one) and a wrong merge (split combine).
+"""
+import cmath
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "deepseek_v2_dims.json")
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _tiny(seed=0, L=5, n_h=2, d_h=4, d_c=8, d_r=4, M=1):
+    rng = np.random.default_rng(seed)
+    return dict(
+        c_kv=_rand(rng, L, d_c), k_r=_rand(rng, L, d_r),
+        q_nope=_rand(rng, M, n_h, d_h), q_rope=_rand(rng, M, n_h, d_r),
+        w_uk=_rand(rng, n_h, d_h, d_c) / math.sqrt(d_c),
+        w_uv=_rand(rng, n_h, d_h, d_c) / math.sqrt(d_c),
+    )
+
+
+# --------------------------------------------------------------------------- RoPE
+
+def _rope_complex(x, pos, base):
+    """RoPE written with complex numbers: pair k is the complex number
+    x[2k] + i x[2k+1], multiplied by exp(i pos theta_k), theta_k = base^(-2k/d)."""
+    d = len(x)
+    out = []
+    for k in range(d // 2):
+        z = complex(x[2 * k], x[2 * k + 1]) * cmath.exp(1j * pos * base ** (-2.0 * k / d))
+        out += [z.real, z.imag]
+    return np.array(out)
+
+
+def test_rope_matches_complex_form():
+    rng = np.random.default_rng(1)
+    for pos in [0, 1, 7, 1000, 131071]:
+        x = rng.standard_normal(64)
+        np.testing.assert_allclose(orc.rope_rotate(x, pos, 10000.0),
+                                   _rope_complex(x, pos, 10000.0), rtol=0,
+                                   atol=1e-12 * max(1, pos))   # angle ulp grows with pos
+
+
+def test_rope_position_zero_is_identity_and_norm_is_kept():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((3, 64))
+    np.testing.assert_array_equal(orc.rope_rotate(x, np.zeros(3), 10000.0), x)
+    y = orc.rope_rotate(x, np.array([5, 4096, 131071]), 10000.0)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+
+
+def test_rope_first_pair_turns_by_pos_radians():
+    # theta_0 = base^0 = 1: the first pair of e_0 lands on (cos p, sin p).
+    e0 = np.zeros(8)
+    e0[0] = 1.0
+    for p in [1, 2, 3, 100]:
+        y = orc.rope_rotate(e0, p, 10000.0)
+        np.testing.assert_allclose(y[:2], [math.cos(p), math.sin(p)], atol=1e-14)
+        assert np.all(y[2:] == 0)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    # blog §2.2.2: (R_m q)^T (R_n k) = q^T R_{n-m} k depends on n - m only.
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    for m, n in [(0, 5), (17, 300), (1000, 999)]:
+        ref = orc.rope_rotate(q, m, 10000.0) @ orc.rope_rotate(k, n, 10000.0)
+        for shift in [1, 123, 65536]:
+            got = orc.rope_rotate(q, m + shift, 10000.0) @ orc.rope_rotate(k, n + shift, 10000.0)
+            assert abs(got - ref) < 1e-9 * (1 + abs(ref))
+
+
+def test_rope_composes_additively():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(64)
+    np.testing.assert_allclose(orc.rope_rotate(orc.rope_rotate(x, 300, 1e4), 45, 1e4),
+                               orc.rope_rotate(x, 345, 1e4), atol=1e-12)
+
+
+# ------------------------------------------------------------ brute-force naive MLA
+
+def _brute_force(c_kv, k_r, q_nope, q_rope, w_uk, w_uv, key_pos, q_pos, n_vis, scale, base):
+    """Scalar loops in float64: eq. 10/11 per element, RoPE in complex form,
+    softmax with math.exp."""
+    M, n_h, d_h = q_nope.shape
+    L, d_c = c_kv.shape
+    out = np.zeros((M, n_h, d_h))
+    lse = np.full((M, n_h), -math.inf)
+    for m in range(M):
+        qr_all = [_rope_complex(q_rope[m, i], q_pos[m], base) for i in range(n_h)]
+        for i in range(n_h):
+            n = int(n_vis[m])
+            scores, values = [], []
+            for j in range(n):
+                kc = [sum(w_uk[i, a, c] * c_kv[j, c] for c in range(d_c)) for a in range(d_h)]
+                vc = [sum(w_uv[i, a, c] * c_kv[j, c] for c in range(d_c)) for a in range(d_h)]
+                kr = _rope_complex(k_r[j], key_pos[j], base)
+                dot = sum(q_nope[m, i, a] * kc[a] for a in range(d_h))
+                dot += sum(qr_all[i][a] * kr[a] for a in range(len(kr)))
+                scores.append(dot * scale)
+                values.append(vc)
+            if n == 0:
+                continue
+            mx = max(scores)
+            es = [math.exp(s - mx) for s in scores]
+            z = sum(es)
+            for a in range(d_h):
+                out[m, i, a] = sum(es[j] * values[j][a] for j in range(n)) / z
+            lse[m, i] = mx + math.log(z)
+    return out, lse
+
+
+@pytest.mark.parametrize("seed,L,M", [(0, 5, 1), (1, 9, 3), (2, 1, 1)])
+def test_naive_matches_brute_force(seed, L, M):
+    t = _tiny(seed=seed, L=L, M=M)
+    key_pos = np.arange(L)
+    q_pos = np.arange(L - M, L) if M > 1 else np.array([L])
+    n_vis = orc.visible_keys(L, M) if M > 1 else np.array([L])
+    scale = 1 / math.sqrt(4 + 4)
+    out, lse, _ = orc.mla_attention_naive(**t, key_pos=key_pos, q_pos=q_pos, n_visible=n_vis,
+                                          scale=scale, base=10000.0)
+    bo, bl = _brute_force(t["c_kv"], t["k_r"], t["q_nope"], t["q_rope"], t["w_uk"], t["w_uv"],
+                          key_pos, q_pos, n_vis, scale, 10000.0)
+    np.testing.assert_allclose(out, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_absorbed_equals_non_absorbed():
+    # Associativity (blog §2.2.1.1): W^UK folds into the query, W^UV into the output.
+    for seed, L, M in [(5, 37, 1), (6, 20, 4)]:
+        t = _tiny(seed=seed, L=L, M=M, n_h=3, d_h=6, d_c=10, d_r=4)
+        q_pos = np.arange(L - M, L) if M > 1 else np.array([L])
+        n_vis = orc.visible_keys(L, M) if M > 1 else np.array([L])
+        scale = 1 / math.sqrt(6 + 4)
+        out, lse, o_lat = orc.mla_attention_naive(**t, key_pos=np.arange(L), q_pos=q_pos,
+                                                  n_visible=n_vis, scale=scale, base=10000.0)
+        rows = orc.kv_cache_rows(t["c_kv"], t["k_r"], np.arange(L), 10000.0)
+        q_lat = orc.absorb_query(t["q_nope"], t["q_rope"], t["w_uk"], q_pos, 10000.0)
+        o_lat2, lse2 = orc.latent_attention(q_lat, rows, n_vis, scale, d_c=10)
+        out2 = orc.out_projection(o_lat2, t["w_uv"])
+        np.testing.assert_allclose(out2, out, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(lse2, lse, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(o_lat2, o_lat, rtol=1e-10, atol=1e-12)
+
+
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(7)
+    s = rng.standard_normal((4, 50)) * 10
+    p, lse = orc._softmax_two_pass(s)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    np.testing.assert_allclose(np.exp(s - lse[:, None]).sum(axis=1), 1.0, atol=1e-12)
+    assert (p >= 0).all()
+
+
+# ------------------------------------------------------------- special cases
+
+def test_identity_weights_reduce_to_library_attention():
+    """W^UK = W^UV = I with d_c = d_h and no RoPE part: MQA over K = V = c^KV
+    (blog §2.1.2: MQA shares one key and value head across all query heads).
+    With one head it is plain scaled-dot attention, checked against torch."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(8)
+    L, d = 23, 16
+    c = rng.standard_normal((L, d))
+    q = rng.standard_normal((1, 1, d))
+    eye = np.eye(d)[None]
+    out, lse, _ = orc.mla_attention_naive(
+        c, np.zeros((L, 0)), q, np.zeros((1, 1, 0)), eye, eye, np.arange(L), np.array([L]),
+        np.array([L]), scale=1 / math.sqrt(d), base=10000.0)
+    tq = torch.tensor(q[0][None], dtype=torch.float64)            # [1, 1, d]
+    tk = torch.tensor(c[None], dtype=torch.float64)               # [1, L, d]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tk)
+    np.testing.assert_allclose(out[0, 0], ref[0, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_single_key_returns_its_value():
+    t = _tiny(seed=9, L=1)
+    out, _, _ = orc.mla_attention_naive(**t, key_pos=[0], q_pos=[1], n_visible=[1],
+                                        scale=0.3, base=10000.0)
+    for i in range(2):
+        np.testing.assert_allclose(out[0, i], t["w_uv"][i] @ t["c_kv"][0], rtol=1e-13)
+
+
+def test_zero_query_averages_values():
+    t = _tiny(seed=10, L=11)
+    t["q_nope"][:] = 0
+    t["q_rope"][:] = 0
+    out, lse, _ = orc.mla_attention_naive(**t, key_pos=np.arange(11), q_pos=[11],
+                                          n_visible=[11], scale=0.3, base=10000.0)
+    for i in range(2):
+        np.testing.assert_allclose(out[0, i], (t["c_kv"] @ t["w_uv"][i].T).mean(axis=0),
+                                   rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, math.log(11), rtol=1e-14)
+
+
+def test_causal_chunk_rows_see_their_own_position():
+    # A chunk of q_len rows at positions L-q_len..L-1: row m sees keys with
+    # position <= its own (eq. 7's sum over j <= t).
+    L, q = 10, 4
+    vis = orc.visible_keys(L, q)
+    q_pos = np.arange(L - q, L)
+    for m in range(q):
+        assert vis[m] == q_pos[m] + 1
+    assert list(orc.visible_keys(7, 1)) == [7]
+
+
+def test_empty_row_gives_zero_and_minus_inf():
+    t = _tiny(seed=11, L=4)
+    out, lse, o_lat = orc.mla_attention_naive(**t, key_pos=np.arange(4), q_pos=[0],
+                                              n_visible=[0], scale=0.3, base=1e4)
+    assert np.all(out == 0) and np.all(o_lat == 0) and np.all(np.isneginf(lse))
+
+
+# ---------------------------------------------------------------- split / combine
+
+@pytest.mark.parametrize("n,S", [(1, 1), (64, 1), (65, 2), (4096, 8), (300, 16), (131072, 64),
+                                 (1000, 3), (0, 4)])
+def test_split_ranges_partition_the_keys(n, S):
+    r = orc.split_ranges(n, 64, S)
+    assert len(r) == S
+    covered = [j for lo, hi in r for j in range(lo, hi)]
+    assert covered == list(range(n))
+    nblk = -(-n // 64)
+    c = -(-nblk // S) if nblk else 0
+    for lo, hi in r:
+        assert hi - lo <= c * 64
+        assert lo % 64 == 0 or lo == n
+
+
+def test_split_ranges_against_block_walk():
+    # Independent formulation: hand out blocks one by one, c to a split.
+    for n in [1, 63, 64, 65, 777, 8192, 8191]:
+        for S in [1, 2, 3, 5, 8, 64]:
+            nblk = -(-n // 64)
+            c = -(-nblk // S)
+            owner = [b // c for b in range(nblk)]
+            want = []
+            for s in range(S):
+                blocks = [b for b in range(nblk) if owner[b] == s]
+                if blocks:
+                    want.append((blocks[0] * 64, min((blocks[-1] + 1) * 64, n)))
+                else:
+                    want.append(None)
+            got = orc.split_ranges(n, 64, S)
+            for w, g in zip(want, got):
+                if w is None:
+                    assert g[0] == g[1]
+                else:
+                    assert w == g
+
+
+def test_combine_of_splits_equals_unsplit():
+    rng = np.random.default_rng(12)
+    L, n_h, W, d_c = 300, 3, 12, 8
+    rows = rng.standard_normal((L, W))
+    q = rng.standard_normal((1, n_h, W))
+    o_full, lse_full = orc.latent_attention(q, rows, [L], 0.4, d_c)
+    for S in [1, 2, 5, 7]:
+        parts = orc.split_ranges(L, 64, S)
+        os_, ls_ = [], []
+        for lo, hi in parts:
+            o, l = orc.latent_attention(q, rows[lo:hi], [hi - lo], 0.4, d_c)
+            os_.append(o)
+            ls_.append(l)
+        o, l = orc.combine_splits(np.stack(os_), np.stack(ls_))
+        np.testing.assert_allclose(o, o_full, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(l, lse_full, rtol=1e-13)
+
+
+def test_combine_all_empty():
+    o, l = orc.combine_splits(np.zeros((3, 1, 2, 4)), np.full((3, 1, 2), -np.inf))
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+# ------------------------------------------------------------- cache-size facts
+
+def test_cached_row_width_is_dc_plus_dr_and_equals_gqa_225_groups():
+    g = json.load(open(GOLDEN))
+    v2 = g["deepseek_v2"]
+    d_c, d_r, d_h, n_h = v2["d_c"], v2["d_R"], v2["d_h"], v2["n_h"]
+    assert d_c == g["relations"]["d_c_over_d_h"] * d_h
+    assert d_r == g["relations"]["d_R_over_d_h"] * d_h
+    rng = np.random.default_rng(13)
+    rows = orc.kv_cache_rows(rng.standard_normal((3, d_c)), rng.standard_normal((3, d_r)),
+                             np.arange(3), 10000.0)
+    per_token = rows.shape[1]
+    # GQA with n_g groups caches 2 n_g d_h elements per token per layer.
+    assert per_token == 2 * g["relations"]["gqa_groups_equivalent"] * d_h
+    # MHA caches 2 n_h d_h (blog §2.1.1); MLA's share of it at the V2 shape:
+    assert abs(per_token / (2 * n_h * d_h) - 576 / 32768) < 1e-15
+    lite = g["deepseek_v2_lite"]
+    assert (lite["d_c"], lite["d_R"], lite["d_h"]) == (d_c, d_r, d_h)
+
+
+def test_cached_rows_keep_latent_unrotated():
+    rng = np.random.default_rng(14)
+    c, k = rng.standard_normal((5, 8)), rng.standard_normal((5, 4))
+    rows = orc.kv_cache_rows(c, k, np.arange(5) + 100, 10000.0)
+    np.testing.assert_array_equal(rows[:, :8], c)
+    np.testing.assert_allclose(rows[:, 8:], orc.rope_rotate(k, np.arange(5) + 100, 1e4))
