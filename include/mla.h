@@ -1,0 +1,206 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) Multi-head Latent Attention hot path.
+ *
+ * The method (DeepSeek-V2 MLA) caches, per token, one joint KV latent
+ * c^KV = W^DKV h (width d_c = 512) and one decoupled RoPE key k^R shared by
+ * all heads (width d_R = 64), instead of per-head keys and values
+ * ("A. Conclusion, Limitation, and Future" DeepSeek-V2 notes,
+ * irregular6612.github.io, §2.1.2 eq. 9-11; DeepSeek-V2 MLA blog,
+ * adg.csdn.net, part 2 §2.2.2).  Attention is evaluated in the weight-absorbed
+ * form: W^UK is folded into the query, W^UV is applied after the softmax sum
+ * (same blog, §2.2.1.1 and §2.2.2: by associativity neither keys nor values
+ * need to be materialised).  Per query row t and head i:
+ *
+ *   q_lat_i = [ W^UK_i^T q_nope_i ; R_{pos t} q_rope_i ]           (576)
+ *   row_j   = [ c^KV_j ; R_{pos j} k_rope_j ]                       (576, cached)
+ *   s_ij    = scale * q_lat_i . row_j
+ *   o_lat_i = sum_j softmax_j(s_ij) c^KV_j                           (512)
+ *   o_i     = W^UV_i o_lat_i                                         (128)
+ *
+ * which equals eq. 7 ("standard MHA" softmax attention, §2.1.1 of the notes)
+ * applied to the per-head keys [W^UK_i c^KV_j ; k^R_j] and values W^UV_i c^KV_j.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Widths are fixed by the pages for both DeepSeek-V2 and V2-Lite: d_c = 512,
+ *   d_R = 64, d_h = 128 (blog part 2 §3.1.1 and the V2-Lite description).
+ * - dtype: MLA_F32 (IEEE float) or MLA_BF16 (bfloat16 as raw 16-bit words).
+ *   Arithmetic is fp32 in both cases (products of bf16 operands are exact in
+ *   fp32; sums accumulate in fp32).  o_lat, lse, partials and the output are
+ *   always fp32.
+ * - RoPE (reading of blog §2.2.2, which only fixes R_m^T R_n = R_{n-m}): adjacent
+ *   element pairs (x[2k], x[2k+1]) are rotated by angle pos * base^(-2k/64),
+ *   k = 0..31; angles are formed in float64.
+ * - Paged cache: kv_cache is [num_blocks, block_size, 576] elements of dtype,
+ *   rows contiguous (a bf16 row is 1152 bytes = 72 x 16 bytes).  Token j of
+ *   sequence b lives in block block_table[b * max_blocks + j / block_size],
+ *   row j % block_size.  block_size must be 64.
+ * - Pointers named "device" are HIP device memory owned by the caller; the
+ *   library never allocates, frees or synchronises.  "host" pointers are read
+ *   or written synchronously during the call.
+ * - stream: a hipStream_t (NULL = the null stream).  Every device call only
+ *   enqueues work on it and returns.
+ * - Errors: argument checks (null pointers, sizes, alignment, dtype) happen on
+ *   the host before anything is enqueued and return a status != MLA_OK with
+ *   nothing enqueued.  A failed launch returns MLA_ERR_HIP.  Device-resident
+ *   integers (block ids, lengths, positions) cannot be checked on the host;
+ *   the kernels skip entries that point outside the cache (a block id outside
+ *   [0, num_blocks) contributes no keys and receives no rows) instead of
+ *   faulting.  No C++ exception crosses this interface.  All entry points are
+ *   thread-safe: the library holds no mutable global state.
+ */
+#ifndef MLA_LATENT_KV_MLA_H
+#define MLA_LATENT_KV_MLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+#define MLA_D_C 512
+#define MLA_D_R 64
+#define MLA_D_H 128
+#define MLA_ROW 576
+#define MLA_BLOCK 64
+
+enum mla_dtype { MLA_F32 = 0, MLA_BF16 = 1 };
+
+enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,   /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,  /* a size is out of range or inconsistent */
+  MLA_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
+  MLA_ERR_DTYPE = 4,  /* unknown dtype */
+  MLA_ERR_HIP = 5     /* the HIP runtime refused a launch */
+};
+
+/* Static text for a status code (never NULL). */
+const char* mla_status_string(int32_t status);
+
+/* MLA_ABI_VERSION of the loaded library. */
+int32_t mla_abi_version(void);
+
+/*
+ * mla_kv_append - write n new tokens into the paged latent cache.
+ *
+ * The cache keeps c^KV unrotated and k^R already rotated at the token's
+ * position, so attention needs no key RoPE (blog part 2 §2.2.2: the RoPE'd key
+ * part is cached; RoPE may not touch the compressed latent).  For r < n:
+ *   slot  = block_table[seq_idx[r] * max_blocks + pos[r] / 64] * 64 + pos[r] % 64
+ *   cache[slot] = [ c_kv[r, 0:512] ; R_{pos[r]} k_rope[r, 0:64] ]
+ * The RoPE position of a token is its index in its sequence.
+ *
+ * kv_cache    device, [num_blocks, 64, 576] dtype, 16-byte aligned (written)
+ * block_table device, int32 [num_seqs, max_blocks]
+ * c_kv        device, [n, 512] dtype (contiguous)
+ * k_rope      device, [n, 64] dtype, before rotation
+ * seq_idx     device, int32 [n]; pos device, int32 [n] (>= 0)
+ * Rows whose seq_idx is outside [0, num_seqs), whose pos < 0 or
+ * pos / 64 >= max_blocks, or whose block id is outside [0, num_blocks) are not
+ * written.  Two rows aimed at one slot race.
+ * n == 0 is a no-op.
+ */
+int32_t mla_kv_append(void* kv_cache, int32_t dtype, int32_t num_blocks, int32_t block_size,
+                      const int32_t* block_table, int32_t num_seqs, int32_t max_blocks,
+                      const void* c_kv, const void* k_rope,
+                      const int32_t* seq_idx, const int32_t* pos, int32_t n,
+                      float rope_base, void* stream);
+
+/*
+ * mla_absorb_q - latent-space queries (W^UK absorbed into the query).
+ *
+ * For every row t < T and head i < n_h:
+ *   q_lat[t, i, 0:512]   = W^UK_i^T q_nope[t, i, :]      (eq. 10 moved to the query)
+ *   q_lat[t, i, 512:576] = R_{q_pos[t]} q_rope[t, i, :]  (decoupled RoPE query)
+ * w_uk holds W^UK as [n_h, 128, 512]: head i's block is rows i*128..(i+1)*128
+ * of eq. 10's matrix (eq. 4-6 head ordering).  Accumulation is fp32; q_lat is
+ * rounded to dtype (round to nearest even for bf16).
+ *
+ * q_nope device [T, n_h, 128]; q_rope device [T, n_h, 64]; w_uk device
+ * [n_h, 128, 512]; q_pos device int32 [T]; q_lat device out [T, n_h, 576];
+ * all of dtype except q_pos, all contiguous and 16-byte aligned.
+ * n_h must be a multiple of 16.  T == 0 is a no-op.
+ */
+int32_t mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
+                     const int32_t* q_pos, int32_t T, int32_t n_h, int32_t dtype,
+                     float rope_base, void* q_lat, void* stream);
+
+/*
+ * mla_decode_paged - attention of latent queries over the paged cache.
+ *
+ * Query rows: q_lat [B, q_len, n_h, 576] (dtype).  Row m of sequence b sees
+ * keys j < seq_lens[b] - (q_len - 1 - m): with q_len == 1 a decode query
+ * sees all seq_lens[b] cached keys; with q_len > 1 (chunked prefill) the chunk
+ * is the last q_len keys and each row sees keys up to its own position
+ * (eq. 7's sum over j <= t).  seq_lens[b] is clamped to max_blocks * 64.
+ *   s_j = softmax_scale * q_lat . row_j; o_lat = sum_j softmax_j(s) row_j[0:512]
+ *   lse = log sum_j exp(s_j)   (natural log; -inf and o_lat = 0 for a row
+ *                                that sees no key)
+ *
+ * Split-KV: with num_splits = S > 1 each row's keys are cut as in
+ * mla_split_plan (per sequence, on seq_lens[b]; a row's range is further cut
+ * at its own visible length) and every split writes its normalised partial
+ * o_part [B, S, q_len, n_h, 512] and lse_part [B, S, q_len, n_h] (fp32);
+ * o_lat/lse are then not written (run mla_splitkv_combine).  With S == 1
+ * o_part/lse_part may be NULL and o_lat [B, q_len, n_h, 512], lse
+ * [B, q_len, n_h] are written directly.
+ *
+ * n_h must be 16, 32, 64 or a multiple of 128.  q_lat and kv_cache must be
+ * 16-byte aligned.  softmax_scale is taken as given; the pages' reading is
+ * 1/sqrt(d_h + d_R) = 1/sqrt(192), the width of the concatenated query/key.
+ */
+int32_t mla_decode_paged(const void* q_lat, const void* kv_cache, int32_t num_blocks,
+                         int32_t block_size, const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t n_h,
+                         int32_t dtype, float softmax_scale, int32_t num_splits,
+                         float* o_part, float* lse_part, float* o_lat, float* lse,
+                         void* stream);
+
+/*
+ * mla_splitkv_combine - merge split-KV partials.
+ *
+ * Softmax over a partition of the keys is recovered exactly from per-split
+ * normalised outputs and log-sum-exps:
+ *   LSE = log sum_s exp(lse_s),  o = sum_s exp(lse_s - LSE) o_s.
+ * Splits with lse_s = -inf carry weight 0; if every split is empty, o = 0 and
+ * LSE = -inf.  o_part device fp32 [B, S, q_len, n_h, 512]; lse_part device fp32
+ * [B, S, q_len, n_h]; o_lat device out fp32 [B, q_len, n_h, 512]; lse device
+ * out fp32 [B, q_len, n_h] (may be NULL).
+ */
+int32_t mla_splitkv_combine(const float* o_part, const float* lse_part, int32_t B, int32_t S,
+                            int32_t q_len, int32_t n_h, float* o_lat, float* lse, void* stream);
+
+/*
+ * mla_out_proj - per-head output o_i = W^UV_i o_lat_i (eq. 11's W^UV applied
+ * after the softmax sum; the result is eq. 7's per-head output, the input of
+ * eq. 8's W^O, which is not applied here).
+ *
+ * o_lat device fp32 [T, n_h, 512]; w_uv device [n_h, 128, 512] dtype (head i's
+ * block is rows i*128..(i+1)*128 of eq. 11's matrix); out device fp32
+ * [T, n_h, 128].  For bf16 weights o_lat is split as hi + lo with
+ * hi = bf16(x), lo = bf16(x - hi), so 16 significant bits of o_lat enter the
+ * product instead of 8.
+ * n_h must be a multiple of 16.  T == 0 is a no-op.
+ */
+int32_t mla_out_proj(const float* o_lat, const void* w_uv, int32_t T, int32_t n_h,
+                     int32_t dtype, float* out, void* stream);
+
+/*
+ * mla_split_plan - the split-KV key ranges, on the host.
+ *
+ * For sequence b with L = seq_lens[b] keys and nblk = ceil(L / 64) blocks,
+ * c = ceil(nblk / S); split s covers keys [min(s*c*64, L), min((s+1)*c*64, L)).
+ * begin_end (host, int32 [B, S, 2]) receives the ranges; empty splits have
+ * begin == end.  seq_lens host int32 [B], each >= 0.
+ */
+int32_t mla_split_plan(const int32_t* seq_lens, int32_t B, int32_t block_size, int32_t num_splits,
+                       int32_t* begin_end);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_LATENT_KV_MLA_H */

@@ -1,0 +1,241 @@
+"""Thin ctypes binding of libmla_latent_kv.so (include/mla.h).
+
+Argument marshalling only: tensors become raw device pointers, the stream is
+torch's current HIP stream, and a non-OK status raises MLAError.  Every
+computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libmla_latent_kv.so")
+
+MLA_F32, MLA_BF16 = 0, 1
+MLA_OK = 0
+D_C, D_R, D_H, ROW, BLOCK = 512, 64, 128, 576, 64
+
+_EXPORTS = ("mla_status_string", "mla_abi_version", "mla_kv_append", "mla_absorb_q",
+            "mla_decode_paged", "mla_splitkv_combine", "mla_out_proj", "mla_split_plan")
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+
+
+def lib_path() -> str:
+    return LIB
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is missing: build it first "
+                           "(python -m mla_latent_kv_04_amd.build)")
+    lib = ctypes.CDLL(LIB)
+    sig = {
+        "mla_status_string": (ctypes.c_char_p, [_I]),
+        "mla_abi_version": (_I, []),
+        "mla_kv_append": (_I, [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I, _F, _P]),
+        "mla_absorb_q": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P]),
+        "mla_decode_paged": (_I, [_P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F, _I,
+                                  _P, _P, _P, _P, _P]),
+        "mla_splitkv_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
+        "mla_out_proj": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+        "mla_split_plan": (_I, [_P, _I, _I, _I, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    return _EXPORTS
+
+
+def _check(fn: str, status: int):
+    if status != MLA_OK:
+        raise MLAError(fn, status, load().mla_status_string(status).decode())
+
+
+def status_string(status: int) -> str:
+    return load().mla_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MLA_F32
+    if t.dtype == torch.bfloat16:
+        return MLA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name: str, dtype=None):
+    """Pointer of a contiguous CUDA(HIP) tensor, or None."""
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def mla_kv_append(kv_cache, block_table, c_kv, k_rope, seq_idx, pos, rope_base=10000.0,
+                  stream=None):
+    """Write rows [c_kv ; R_pos k_rope] into the paged cache (see mla.h)."""
+    torch = _torch()
+    dt = _dtype_code(kv_cache)
+    n = int(c_kv.shape[0]) if c_kv is not None else 0
+    for name, t in (("c_kv", c_kv), ("k_rope", k_rope)):
+        if t.dtype != kv_cache.dtype:
+            raise TypeError(f"{name} dtype differs from the cache")
+    if tuple(c_kv.shape) != (n, D_C) or tuple(k_rope.shape) != (n, D_R):
+        raise ValueError("c_kv must be [n, 512] and k_rope [n, 64]")
+    if tuple(seq_idx.shape) != (n,) or tuple(pos.shape) != (n,):
+        raise ValueError("seq_idx and pos must be [n]")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != ROW:
+        raise ValueError("kv_cache must be [num_blocks, 64, 576]")
+    st = load().mla_kv_append(
+        _dev(kv_cache, "kv_cache"), dt, int(kv_cache.shape[0]), int(kv_cache.shape[1]),
+        _dev(block_table, "block_table", torch.int32), int(block_table.shape[0]),
+        int(block_table.shape[1]), _dev(c_kv, "c_kv"), _dev(k_rope, "k_rope"),
+        _dev(seq_idx, "seq_idx", torch.int32), _dev(pos, "pos", torch.int32), n,
+        float(rope_base), _stream(stream))
+    _check("mla_kv_append", st)
+
+
+def mla_absorb_q(q_nope, q_rope, w_uk, q_pos, q_lat, rope_base=10000.0, stream=None):
+    """q_lat = [W^UK^T q_nope ; R q_rope] per row and head (see mla.h)."""
+    torch = _torch()
+    dt = _dtype_code(q_nope)
+    T, n_h = int(q_nope.shape[0]), int(q_nope.shape[1])
+    if tuple(q_nope.shape) != (T, n_h, D_H) or tuple(q_rope.shape) != (T, n_h, D_R):
+        raise ValueError("q_nope must be [T, n_h, 128] and q_rope [T, n_h, 64]")
+    if tuple(w_uk.shape) != (n_h, D_H, D_C) or tuple(q_lat.shape) != (T, n_h, ROW):
+        raise ValueError("w_uk must be [n_h, 128, 512] and q_lat [T, n_h, 576]")
+    for name, t in (("q_rope", q_rope), ("w_uk", w_uk), ("q_lat", q_lat)):
+        if t.dtype != q_nope.dtype:
+            raise TypeError(f"{name} dtype differs from q_nope")
+    st = load().mla_absorb_q(_dev(q_nope, "q_nope"), _dev(q_rope, "q_rope"), _dev(w_uk, "w_uk"),
+                             _dev(q_pos, "q_pos", torch.int32), T, n_h, dt, float(rope_base),
+                             _dev(q_lat, "q_lat"), _stream(stream))
+    _check("mla_absorb_q", st)
+
+
+def mla_decode_paged(q_lat, kv_cache, block_table, seq_lens, q_len, softmax_scale, num_splits=1,
+                     o_part=None, lse_part=None, o_lat=None, lse=None, stream=None):
+    """Latent attention over the paged cache (see mla.h).  q_lat is [B*q_len, n_h, 576]."""
+    torch = _torch()
+    dt = _dtype_code(q_lat)
+    if kv_cache.dtype != q_lat.dtype:
+        raise TypeError("kv_cache dtype differs from q_lat")
+    B = int(seq_lens.shape[0])
+    n_h = int(q_lat.shape[-2])
+    if q_lat.shape[-1] != ROW or q_lat.numel() != B * q_len * n_h * ROW:
+        raise ValueError("q_lat must hold [B, q_len, n_h, 576]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    rows = B * q_len * n_h
+    if int(num_splits) > 1:
+        if o_part is None or lse_part is None or o_part.numel() != rows * num_splits * D_C \
+                or lse_part.numel() != rows * num_splits:
+            raise ValueError("o_part / lse_part must hold [B, S, q_len, n_h, 512] / [B, S, q_len, n_h]")
+    elif o_lat is None or lse is None or o_lat.numel() != rows * D_C or lse.numel() != rows:
+        raise ValueError("o_lat / lse must hold [B, q_len, n_h, 512] / [B, q_len, n_h]")
+    f32 = torch.float32
+    st = load().mla_decode_paged(
+        _dev(q_lat, "q_lat"), _dev(kv_cache, "kv_cache"), int(kv_cache.shape[0]),
+        int(kv_cache.shape[1]), _dev(block_table, "block_table", torch.int32),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32), B, int(q_len), n_h,
+        dt, float(softmax_scale), int(num_splits), _dev(o_part, "o_part", f32),
+        _dev(lse_part, "lse_part", f32), _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32),
+        _stream(stream))
+    _check("mla_decode_paged", st)
+
+
+def mla_splitkv_combine(o_part, lse_part, B, S, q_len, n_h, o_lat, lse=None, stream=None):
+    """Merge split partials (see mla.h)."""
+    torch = _torch()
+    f32 = torch.float32
+    if o_part.numel() != B * S * q_len * n_h * D_C or lse_part.numel() != B * S * q_len * n_h:
+        raise ValueError("partials have the wrong size")
+    if o_lat.numel() != B * q_len * n_h * D_C:
+        raise ValueError("o_lat has the wrong size")
+    if lse is not None and lse.numel() != B * q_len * n_h:
+        raise ValueError("lse has the wrong size")
+    st = load().mla_splitkv_combine(_dev(o_part, "o_part", f32), _dev(lse_part, "lse_part", f32),
+                                    int(B), int(S), int(q_len), int(n_h),
+                                    _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32),
+                                    _stream(stream))
+    _check("mla_splitkv_combine", st)
+
+
+def mla_out_proj(o_lat, w_uv, out, stream=None):
+    """out[t, i] = W^UV_i o_lat[t, i] (see mla.h).  o_lat [T, n_h, 512] fp32."""
+    torch = _torch()
+    dt = _dtype_code(w_uv)
+    T, n_h = int(o_lat.shape[0]), int(o_lat.shape[1])
+    if tuple(o_lat.shape) != (T, n_h, D_C) or tuple(w_uv.shape) != (n_h, D_H, D_C):
+        raise ValueError("o_lat must be [T, n_h, 512] and w_uv [n_h, 128, 512]")
+    if tuple(out.shape) != (T, n_h, D_H):
+        raise ValueError("out must be [T, n_h, 128]")
+    f32 = torch.float32
+    st = load().mla_out_proj(_dev(o_lat, "o_lat", f32), _dev(w_uv, "w_uv"), T, n_h, dt,
+                             _dev(out, "out", f32), _stream(stream))
+    _check("mla_out_proj", st)
+
+
+def mla_split_plan(seq_lens, num_splits, block_size=BLOCK) -> np.ndarray:
+    """Host split plan: int32 [B, S, 2] key ranges (see mla.h)."""
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    B = int(sl.shape[0])
+    out = np.zeros((B, int(num_splits), 2), dtype=np.int32)
+    st = load().mla_split_plan(sl.ctypes.data_as(ctypes.c_void_p), B, int(block_size),
+                               int(num_splits), out.ctypes.data_as(ctypes.c_void_p))
+    _check("mla_split_plan", st)
+    return out

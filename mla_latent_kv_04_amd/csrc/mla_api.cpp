@@ -1,0 +1,144 @@
+// C ABI entry points (include/mla.h): host-side argument checks, then launch.
+//
+// Every check here runs before anything is enqueued, so a rejected call has
+// no effect on the stream.  No entry point allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool dtype_ok(int32_t dt) { return dt == MLA_F32 || dt == MLA_BF16; }
+
+// Head counts the decode kernels are built for.
+bool decode_heads_ok(int32_t n_h) {
+  return n_h == 16 || n_h == 32 || n_h == 64 || (n_h > 0 && n_h % 128 == 0);
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MLA_ERR_DTYPE: return "unknown dtype";
+    case MLA_ERR_HIP: return "the HIP runtime refused a launch";
+    default: return "unknown status";
+  }
+}
+
+int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+int32_t mla_kv_append(void* kv_cache, int32_t dtype, int32_t num_blocks, int32_t block_size,
+                      const int32_t* block_table, int32_t num_seqs, int32_t max_blocks,
+                      const void* c_kv, const void* k_rope, const int32_t* seq_idx,
+                      const int32_t* pos, int32_t n, float rope_base, void* stream) {
+  if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  if (n < 0 || num_blocks < 1 || num_seqs < 1 || max_blocks < 1 || block_size != MLA_BLOCK ||
+      !(rope_base > 0.0f))
+    return MLA_ERR_SHAPE;
+  if (n == 0) return MLA_OK;
+  if (!kv_cache || !block_table || !c_kv || !k_rope || !seq_idx || !pos) return MLA_ERR_NULL;
+  if (!aligned16(kv_cache) || !aligned16(c_kv) || !aligned4(k_rope)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_kv_append(kv_cache, dtype, num_blocks, block_table, num_seqs,
+                                          max_blocks, c_kv, k_rope, seq_idx, pos, n, rope_base,
+                                          (hipStream_t)stream));
+}
+
+int32_t mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
+                     const int32_t* q_pos, int32_t T, int32_t n_h, int32_t dtype,
+                     float rope_base, void* q_lat, void* stream) {
+  if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  if (T < 0 || n_h < 16 || n_h % 16 != 0 || !(rope_base > 0.0f)) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!q_nope || !q_rope || !w_uk || !q_pos || !q_lat) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat) || !aligned4(q_rope))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_absorb_q(q_nope, q_rope, w_uk, q_pos, T, n_h, dtype, rope_base,
+                                         q_lat, (hipStream_t)stream));
+}
+
+int32_t mla_decode_paged(const void* q_lat, const void* kv_cache, int32_t num_blocks,
+                         int32_t block_size, const int32_t* block_table, int32_t max_blocks,
+                         const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t n_h,
+                         int32_t dtype, float softmax_scale, int32_t num_splits, float* o_part,
+                         float* lse_part, float* o_lat, float* lse, void* stream) {
+  if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  if (B < 0 || q_len < 1 || num_blocks < 1 || max_blocks < 1 || block_size != MLA_BLOCK ||
+      !decode_heads_ok(n_h) || num_splits < 1 || !(softmax_scale > 0.0f))
+    return MLA_ERR_SHAPE;
+  // grid.x = B * q_len * num_splits must fit the launch limit
+  if ((int64_t)B * q_len * num_splits > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q_lat || !kv_cache || !block_table || !seq_lens) return MLA_ERR_NULL;
+  float* o_out = o_lat;
+  float* l_out = lse;
+  if (num_splits > 1) {
+    if (!o_part || !lse_part) return MLA_ERR_NULL;
+    o_out = o_part;
+    l_out = lse_part;
+  } else if (!o_lat || !lse) {
+    return MLA_ERR_NULL;
+  }
+  if (!aligned16(q_lat) || !aligned16(kv_cache) || !aligned16(o_out) || !aligned4(l_out))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_decode(q_lat, kv_cache, num_blocks, block_table, max_blocks,
+                                       seq_lens, B, q_len, n_h, dtype, softmax_scale, num_splits,
+                                       o_out, l_out, (hipStream_t)stream));
+}
+
+int32_t mla_splitkv_combine(const float* o_part, const float* lse_part, int32_t B, int32_t S,
+                            int32_t q_len, int32_t n_h, float* o_lat, float* lse, void* stream) {
+  if (B < 0 || S < 1 || q_len < 1 || n_h < 1) return MLA_ERR_SHAPE;
+  if ((int64_t)B * q_len > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!o_part || !lse_part || !o_lat) return MLA_ERR_NULL;
+  if (!aligned16(o_part) || !aligned16(o_lat) || !aligned4(lse_part) || (lse && !aligned4(lse)))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_combine(o_part, lse_part, B, S, q_len, n_h, o_lat, lse,
+                                        (hipStream_t)stream));
+}
+
+int32_t mla_out_proj(const float* o_lat, const void* w_uv, int32_t T, int32_t n_h, int32_t dtype,
+                     float* out, void* stream) {
+  if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  if (T < 0 || n_h < 1) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_out_proj(o_lat, w_uv, T, n_h, dtype, out, (hipStream_t)stream));
+}
+
+int32_t mla_split_plan(const int32_t* seq_lens, int32_t B, int32_t block_size, int32_t num_splits,
+                       int32_t* begin_end) {
+  if (B < 0 || num_splits < 1 || block_size != MLA_BLOCK) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!seq_lens || !begin_end) return MLA_ERR_NULL;
+  for (int32_t b = 0; b < B; ++b)
+    if (seq_lens[b] < 0) return MLA_ERR_SHAPE;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t L = seq_lens[b];
+    const int64_t nblk = (L + block_size - 1) / block_size;
+    const int64_t c = (nblk + num_splits - 1) / num_splits;
+    for (int32_t s = 0; s < num_splits; ++s) {
+      int64_t lo = s * c * block_size, hi = (s + 1) * c * block_size;
+      if (lo > L) lo = L;
+      if (hi > L) hi = L;
+      begin_end[((int64_t)b * num_splits + s) * 2] = (int32_t)lo;
+      begin_end[((int64_t)b * num_splits + s) * 2 + 1] = (int32_t)hi;
+    }
+  }
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -57,7 +57,7 @@ class Workload:
     block_size: int = BLOCK
     table: str = "permuted"   # "identity" or "permuted"
     seed: int = 0
-    num_splits: int = 1       # split-KV partitions used by the benchmark step
+    num_splits: int = 1       # split-KV partitions of the benchmark's launch
 
 
 # The five workloads: V2-Lite fp32 (tiny), V2-Lite bf16 paged, full V2 ragged
@@ -66,9 +66,9 @@ WORKLOADS = {
     "v2lite_f32_L256": Workload("v2lite_f32_L256", "f32", B=1, n_h=16, ctx=256,
                                 table="identity", seed=1001),
     "v2lite_bf16_B64_L4096": Workload("v2lite_bf16_B64_L4096", "bf16", B=64, n_h=16,
-                                      ctx=4096, seed=1002),
+                                      ctx=4096, seed=1002, num_splits=4),
     "v2_bf16_B128_L1k-8k": Workload("v2_bf16_B128_L1k-8k", "bf16", B=128, n_h=128,
-                                    ctx=(1024, 8192), seed=1003),
+                                    ctx=(1024, 8192), seed=1003, num_splits=2),
     "v2_bf16_B4_L128k_splitkv": Workload("v2_bf16_B4_L128k_splitkv", "bf16", B=4, n_h=128,
                                          ctx=131072, seed=1004, num_splits=64),
     "v2_bf16_prefill_6144+2048": Workload("v2_bf16_prefill_6144+2048", "bf16", B=1,
@@ -159,8 +159,10 @@ def make_problem(wl: Workload, *, B: Optional[int] = None, n_h: Optional[int] = 
         assert seq_lens.shape == (wl.B,)
     else:
         seq_lens = np.full(wl.B, int(wl.ctx), dtype=np.int32)
-    if (seq_lens < wl.q_len).any():
-        raise ValueError("every sequence must hold at least q_len keys")
+    if wl.q_len > 1 and (seq_lens < wl.q_len).any():
+        raise ValueError("a prefill chunk must lie inside its sequence")
+    if (seq_lens < 0).any():
+        raise ValueError("negative context length")
     offsets = np.zeros(wl.B + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(seq_lens.astype(np.int64))
     total = int(offsets[-1])

@@ -1,0 +1,104 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+entry point, rejects bad arguments before enqueuing anything, and its host
+split plan matches the oracle's rule bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_latent_kv_04_amd as pkg
+from mla_latent_kv_04_amd import _binding as B
+from oracle import mla_oracle as orc
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int32_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(B.exported_symbols())
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.mla_abi_version() == 1
+    for s in range(6):
+        assert len(B.status_string(s)) > 0
+    assert B.status_string(99) == "unknown status"
+
+
+NULL = None
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced by rejected calls
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    call = lib.mla_decode_paged
+    ok = dict(q_lat=FAKE, kv=FAKE, nblk=4, bs=64, table=FAKE, maxb=4, sl=FAKE, B=1, q_len=1,
+              n_h=16, dt=1, scale=0.07, S=1, op=NULL, lp=NULL, o=FAKE, l=FAKE)
+
+    def run(**kw):
+        a = dict(ok, **kw)
+        return call(a["q_lat"], a["kv"], a["nblk"], a["bs"], a["table"], a["maxb"], a["sl"],
+                    a["B"], a["q_len"], a["n_h"], a["dt"], a["scale"], a["S"], a["op"], a["lp"],
+                    a["o"], a["l"], None)
+
+    assert run(dt=7) == 4
+    assert run(bs=32) == 2
+    assert run(n_h=48) == 2
+    assert run(n_h=0) == 2
+    assert run(S=0) == 2
+    assert run(q_len=0) == 2
+    assert run(scale=0.0) == 2
+    assert run(q_lat=NULL) == 1
+    assert run(o=NULL) == 1
+    assert run(S=4) == 1                  # split path needs partial buffers
+    assert run(q_lat=MISALIGNED) == 3
+    assert run(B=0) == 0                  # nothing to do
+
+
+def test_other_entry_points_reject_bad_arguments(lib):
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, FAKE, 4, 24, 1, 1e4, FAKE, None) == 2
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, NULL, 4, 16, 1, 1e4, FAKE, None) == 1
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, FAKE, 4, 16, 2, 1e4, FAKE, None) == 4
+    assert lib.mla_absorb_q(FAKE, FAKE, MISALIGNED, FAKE, 4, 16, 1, 1e4, FAKE, None) == 3
+    assert lib.mla_absorb_q(NULL, NULL, NULL, NULL, 0, 16, 1, 1e4, NULL, None) == 0
+    assert lib.mla_kv_append(FAKE, 1, 4, 64, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 0.0, None) == 2
+    assert lib.mla_kv_append(FAKE, 1, 4, 64, NULL, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 1e4, None) == 1
+    assert lib.mla_kv_append(FAKE, 1, 4, 16, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 1e4, None) == 2
+    assert lib.mla_kv_append(MISALIGNED, 1, 4, 64, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 1e4,
+                             None) == 3
+    assert lib.mla_splitkv_combine(FAKE, FAKE, 2, 0, 1, 16, FAKE, FAKE, None) == 2
+    assert lib.mla_splitkv_combine(FAKE, NULL, 2, 2, 1, 16, FAKE, FAKE, None) == 1
+    assert lib.mla_out_proj(FAKE, FAKE, 4, 16, 3, FAKE, None) == 4
+    assert lib.mla_out_proj(NULL, FAKE, 4, 16, 1, FAKE, None) == 1
+    assert lib.mla_out_proj(NULL, NULL, 0, 16, 1, NULL, None) == 0
+
+
+def test_split_plan_matches_oracle_rule():
+    rng = np.random.default_rng(0)
+    lens = np.concatenate([[0, 1, 63, 64, 65, 4096, 131072, 8191],
+                           rng.integers(0, 9000, size=40)]).astype(np.int32)
+    for S in [1, 2, 3, 7, 8, 64, 100]:
+        plan = pkg.mla_split_plan(lens, S)
+        for b, L in enumerate(lens):
+            want = orc.split_ranges(int(L), 64, S)
+            assert [tuple(x) for x in plan[b].tolist()] == want
+
+
+def test_split_plan_rejects_negative_length():
+    with pytest.raises(B.MLAError):
+        pkg.mla_split_plan(np.array([5, -1], dtype=np.int32), 2)
