@@ -123,7 +123,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="v2_bf16_B128_L1k-8k")
-    ap.add_argument("--splits", type=int, default=None, help="split-KV partitions (default: workload's)")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="split-KV partitions per row; 0 = balanced work plan (default: workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -155,7 +156,11 @@ def main():
         mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE)
         if ev is not None:
             ev[0].record(stream)
-        if splits > 1:
+        if splits == 0:
+            mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
+                                         scale, dp.work, dp.o_lat, dp.lse, o_part=dp.o_part,
+                                         lse_part=dp.lse_part)
+        elif splits > 1:
             mla.mla_decode_paged(dp.q_lat, dp.kv_cache, dp.block_table, dp.seq_lens, dp.q_len,
                                  scale, splits, o_part=dp.o_part, lse_part=dp.lse_part)
         else:
@@ -163,7 +168,11 @@ def main():
                                  scale, 1, o_lat=dp.o_lat, lse=dp.lse)
         if ev is not None:
             ev[1].record(stream)
-        if splits > 1:
+        if splits == 0:
+            if dp.split.shape[0] > 0:
+                mla.mla_combine_planned(dp.o_part, dp.lse_part, dp.split, dp.n_h, dp.o_lat,
+                                        dp.lse)
+        elif splits > 1:
             mla.mla_splitkv_combine(dp.o_part, dp.lse_part, dp.B, splits, dp.q_len, dp.n_h,
                                     dp.o_lat, dp.lse)
         mla.mla_out_proj(dp.o_lat, dp.w_uv, dp.out)
@@ -208,7 +217,10 @@ def main():
 
     cfg = {"workload": wl.name, "B": wl.B, "n_h": wl.n_h, "q_len": wl.q_len,
            "context": (f"U[{wl.ctx[0]},{wl.ctx[1]}]" if isinstance(wl.ctx, tuple) else wl.ctx),
-           "block_size": wl.block_size, "num_splits": splits, "d_c": 512, "d_R": 64, "d_h": 128}
+           "block_size": wl.block_size,
+           "split_kv": ("balanced plan" if splits == 0 else f"{splits} per row"),
+           "work_items": (int(dp.work.shape[0]) if splits == 0 else dp.B * dp.q_len * splits),
+           "d_c": 512, "d_R": 64, "d_h": 128}
     rec = {
         "metric": "MLA decode tokens/s (+ attention-kernel HBM GB/s and MFMA share of peak), "
                   "DeepSeek-V2 head shape",

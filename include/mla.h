@@ -148,7 +148,7 @@ int32_t mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
  * o_part/lse_part may be NULL and o_lat [B, q_len, n_h, 512], lse
  * [B, q_len, n_h] are written directly.
  *
- * n_h must be 16, 32, 64 or a multiple of 128.  q_lat and kv_cache must be
+ * n_h must be 16, 32 or a multiple of 64.  q_lat and kv_cache must be
  * 16-byte aligned.  softmax_scale is taken as given; the pages' reading is
  * 1/sqrt(d_h + d_R) = 1/sqrt(192), the width of the concatenated query/key.
  */
@@ -198,6 +198,55 @@ int32_t mla_out_proj(const float* o_lat, const void* w_uv, int32_t T, int32_t n_
  */
 int32_t mla_split_plan(const int32_t* seq_lens, int32_t B, int32_t block_size, int32_t num_splits,
                        int32_t* begin_end);
+
+/*
+ * mla_plan_decode - a load-balanced split-KV work list, on the host.
+ *
+ * Rows r = b * q_len + m; row r sees n_r keys (the visibility rule of
+ * mla_decode_paged, with seq_lens[b] clamped at 0) and spans T_r = ceil(n_r / 64)
+ * blocks.  With G = n_h / 64 workgroups per row piece when n_h is a multiple
+ * of 64 (else G = 1) and W = max(1, ceil(G * sum_r T_r / num_slots)) blocks per
+ * piece, row r is cut into P_r = max(1, ceil(T_r / W)) pieces; piece k covers
+ * blocks [floor(k T_r / P_r), floor((k+1) T_r / P_r)), i.e. keys
+ * [64 floor(k T_r / P_r), min(64 floor((k+1) T_r / P_r), n_r)).
+ * Rows with one piece are written straight to o_lat; the pieces of a split
+ * row get consecutive partial slots (rows in increasing order).
+ *
+ *   work  (host out, int32 [n_work, 4]) = {row, key_begin, key_end, slot},
+ *         slot = -1 for an unsplit row; items sorted by decreasing piece size
+ *         (blocks), then row, then piece index, so the longest start first.
+ *   split (host out, int32 [n_split, 3]) = {row, first_slot, count} for every
+ *         split row, in row order; n_parts = number of partial slots.
+ * max_work bounds both arrays; if the plan needs more, MLA_ERR_SHAPE is
+ * returned and *n_work holds the required size.  num_slots: workgroups the
+ * device runs at once (e.g. its compute-unit count).  Pure integer host code.
+ */
+int32_t mla_plan_decode(const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t block_size,
+                        int32_t n_h, int32_t num_slots, int32_t max_work, int32_t* work,
+                        int32_t* n_work, int32_t* split, int32_t* n_split, int32_t* n_parts);
+
+/*
+ * mla_decode_paged_planned - mla_decode_paged over a work list from
+ * mla_plan_decode (copied to the device).  Item i scores its row's query
+ * against keys [key_begin, key_end) of the row's sequence (b = row / q_len)
+ * and writes o_lat/lse row `row` when slot < 0, else o_part/lse_part row
+ * `slot` (fp32 [n_parts, n_h, 512] / [n_parts, n_h]).  Arguments as in
+ * mla_decode_paged; key ranges are clamped to max_blocks * 64.
+ */
+int32_t mla_decode_paged_planned(const void* q_lat, const void* kv_cache, int32_t num_blocks,
+                                 int32_t block_size, const int32_t* block_table,
+                                 int32_t max_blocks, int32_t B, int32_t q_len, int32_t n_h,
+                                 int32_t dtype, float softmax_scale, const int32_t* work,
+                                 int32_t n_work, float* o_part, float* lse_part, float* o_lat,
+                                 float* lse, void* stream);
+
+/*
+ * mla_combine_planned - merge the partials of every split row of a plan
+ * (split device int32 [n_split, 3] from mla_plan_decode), with the same
+ * log-sum-exp rule as mla_splitkv_combine, into o_lat / lse rows.
+ */
+int32_t mla_combine_planned(const float* o_part, const float* lse_part, const int32_t* split,
+                            int32_t n_split, int32_t n_h, float* o_lat, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

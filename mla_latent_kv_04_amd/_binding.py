@@ -19,7 +19,8 @@ MLA_OK = 0
 D_C, D_R, D_H, ROW, BLOCK = 512, 64, 128, 576, 64
 
 _EXPORTS = ("mla_status_string", "mla_abi_version", "mla_kv_append", "mla_absorb_q",
-            "mla_decode_paged", "mla_splitkv_combine", "mla_out_proj", "mla_split_plan")
+            "mla_decode_paged", "mla_splitkv_combine", "mla_out_proj", "mla_split_plan",
+            "mla_plan_decode", "mla_decode_paged_planned", "mla_combine_planned")
 
 
 class MLAError(RuntimeError):
@@ -58,6 +59,10 @@ def load() -> ctypes.CDLL:
         "mla_splitkv_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
         "mla_out_proj": (_I, [_P, _P, _I, _I, _I, _P, _P]),
         "mla_split_plan": (_I, [_P, _I, _I, _I, _P]),
+        "mla_plan_decode": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+        "mla_decode_paged_planned": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _F, _P, _I,
+                                          _P, _P, _P, _P, _P]),
+        "mla_combine_planned": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -239,3 +244,67 @@ def mla_split_plan(seq_lens, num_splits, block_size=BLOCK) -> np.ndarray:
                                int(num_splits), out.ctypes.data_as(ctypes.c_void_p))
     _check("mla_split_plan", st)
     return out
+
+
+def mla_plan_decode(seq_lens, q_len, n_h, num_slots, block_size=BLOCK):
+    """Host work plan (see mla.h).  Returns (work int32 [n, 4], split int32 [k, 3], n_parts)."""
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    B = int(sl.shape[0])
+    n_work, n_split, n_parts = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    cap = 16
+    while True:
+        work = np.zeros((cap, 4), dtype=np.int32)
+        split = np.zeros((cap, 3), dtype=np.int32)
+        st = load().mla_plan_decode(sl.ctypes.data_as(ctypes.c_void_p), B, int(q_len),
+                                    int(block_size), int(n_h), int(num_slots), cap,
+                                    work.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n_work),
+                                    split.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n_split),
+                                    ctypes.byref(n_parts))
+        if st == MLA_OK:
+            return work[:n_work.value].copy(), split[:n_split.value].copy(), int(n_parts.value)
+        if st == 2 and max(n_work.value, n_split.value) > cap:
+            cap = max(n_work.value, n_split.value)
+            continue
+        _check("mla_plan_decode", st)
+
+
+def mla_decode_paged_planned(q_lat, kv_cache, block_table, B, q_len, softmax_scale, work,
+                             o_lat, lse, o_part=None, lse_part=None, stream=None):
+    """Attention over a device work list from mla_plan_decode (see mla.h)."""
+    torch = _torch()
+    dt = _dtype_code(q_lat)
+    if kv_cache.dtype != q_lat.dtype:
+        raise TypeError("kv_cache dtype differs from q_lat")
+    n_h = int(q_lat.shape[-2])
+    rows = int(B) * int(q_len)
+    if q_lat.shape[-1] != ROW or q_lat.numel() != rows * n_h * ROW:
+        raise ValueError("q_lat must hold [B, q_len, n_h, 576]")
+    if work.dim() != 2 or work.shape[1] != 4:
+        raise ValueError("work must be [n_work, 4]")
+    if o_lat.numel() != rows * n_h * D_C or lse.numel() != rows * n_h:
+        raise ValueError("o_lat / lse must hold [B, q_len, n_h, 512] / [B, q_len, n_h]")
+    if o_part is not None and (o_part.shape[-1] != D_C or o_part.numel() % (n_h * D_C) or
+                               lse_part is None or lse_part.numel() * D_C != o_part.numel()):
+        raise ValueError("o_part / lse_part must be [n_parts, n_h, 512] / [n_parts, n_h]")
+    f32 = torch.float32
+    st = load().mla_decode_paged_planned(
+        _dev(q_lat, "q_lat"), _dev(kv_cache, "kv_cache"), int(kv_cache.shape[0]),
+        int(kv_cache.shape[1]), _dev(block_table, "block_table", torch.int32),
+        int(block_table.shape[1]), int(B), int(q_len), n_h, dt, float(softmax_scale),
+        _dev(work, "work", torch.int32), int(work.shape[0]), _dev(o_part, "o_part", f32),
+        _dev(lse_part, "lse_part", f32), _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32),
+        _stream(stream))
+    _check("mla_decode_paged_planned", st)
+
+
+def mla_combine_planned(o_part, lse_part, split, n_h, o_lat, lse=None, stream=None):
+    """Merge the partials of a plan's split rows (see mla.h)."""
+    torch = _torch()
+    f32 = torch.float32
+    if split.dim() != 2 or split.shape[1] != 3:
+        raise ValueError("split must be [n_split, 3]")
+    st = load().mla_combine_planned(_dev(o_part, "o_part", f32), _dev(lse_part, "lse_part", f32),
+                                    _dev(split, "split", torch.int32), int(split.shape[0]),
+                                    int(n_h), _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32),
+                                    _stream(stream))
+    _check("mla_combine_planned", st)

@@ -29,7 +29,7 @@ COMMON = [
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["kv_append.hip", "absorb_q.hip", "decode.hip", "combine.hip", "out_proj.hip",
+SOURCES = ["kv_append.hip", "absorb_q.hip", "decode.hip", "decode_h64.hip", "combine.hip", "out_proj.hip",
            "mla_api.cpp"]
 
 

@@ -46,7 +46,48 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   if (lse != nullptr && d4 == 0) lse[(long)row * n_h + head] = z > 0.0f ? mx + __logf(z) : -INFINITY;
 }
 
+// Planned merge: split[j] = {row, first_slot, count}; partial rows are
+// first_slot .. first_slot + count - 1 of o_part / lse_part ([slots, n_h, ...]).
+__global__ void __launch_bounds__(256) combine_planned_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    const int* __restrict__ split, int n_h, float* __restrict__ o_lat, float* __restrict__ lse) {
+  const int head = blockIdx.y * 2 + (threadIdx.x >> 7);
+  const int d4 = threadIdx.x & 127;
+  if (head >= n_h) return;
+  const int row = split[blockIdx.x * 3], first = split[blockIdx.x * 3 + 1];
+  const int count = split[blockIdx.x * 3 + 2];
+  float mx = -INFINITY;
+  for (int k = 0; k < count; ++k) mx = fmaxf(mx, lse_part[(long)(first + k) * n_h + head]);
+  float4 o = {0, 0, 0, 0};
+  float z = 0.0f;
+  if (mx != -INFINITY) {
+    for (int k = 0; k < count; ++k) {
+      const long pr = (long)(first + k) * n_h + head;
+      const float l = lse_part[pr];
+      if (l == -INFINITY) continue;
+      const float w = __expf(l - mx);
+      z += w;
+      const float4 x = reinterpret_cast<const float4*>(o_part + pr * D_C)[d4];
+      o.x += w * x.x; o.y += w * x.y; o.z += w * x.z; o.w += w * x.w;
+    }
+  }
+  const float inv = z > 0.0f ? 1.0f / z : 0.0f;
+  reinterpret_cast<float4*>(o_lat + ((long)row * n_h + head) * D_C)[d4] =
+      float4{o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+  if (lse != nullptr && d4 == 0) lse[(long)row * n_h + head] = z > 0.0f ? mx + __logf(z) : -INFINITY;
+}
+
 }  // namespace
+
+hipError_t launch_combine_planned(const float* o_part, const float* lse_part, const int* split,
+                                  int n_split, int n_h, float* o_lat, float* lse,
+                                  hipStream_t stream) {
+  if (n_split == 0) return hipSuccess;
+  dim3 grid((unsigned)n_split, (n_h + 1) / 2), block(256);
+  hipLaunchKernelGGL(combine_planned_kernel, grid, block, 0, stream, o_part, lse_part, split, n_h,
+                     o_lat, lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int B, int S, int q_len,
                           int n_h, float* o_lat, float* lse, hipStream_t stream) {

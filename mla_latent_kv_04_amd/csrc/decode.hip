@@ -19,8 +19,6 @@
 // cross-lane permutes); the running max is only moved when a score exceeds it
 // by more than 2^8, so rescaling the accumulators is rare and the result is
 // unchanged (the same reference max is used for the sum and the output).
-#include <type_traits>
-
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -114,24 +112,17 @@ template <class E, class C>
 __global__ void __launch_bounds__(C::THREADS, 1) decode_kernel(
     const typename E::storage* __restrict__ q_lat, const typename E::storage* __restrict__ cache,
     int num_blocks, const int* __restrict__ table, int max_blocks, const int* __restrict__ seq_lens,
-    int q_len, int n_h, float scale_log2, int S, float* __restrict__ o_out,
-    float* __restrict__ lse_out) {
+    int q_len, int n_h, int n_rows, float scale_log2, int S, const int4* __restrict__ work,
+    float* __restrict__ o_lat, float* __restrict__ lse, float* __restrict__ o_part,
+    float* __restrict__ lse_part) {
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
   const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   const int wh = wave % C::NWH, wt = wave / C::NWH;
-  const int item = blockIdx.x;
-  const int s = item % S, bm = item / S, m = bm % q_len, b = bm / q_len;
+  const WorkItem wi = decode_item(blockIdx.x, work, n_rows, q_len, S, seq_lens, max_blocks);
+  if (!wi.valid) return;
+  const int b = wi.b, m = wi.m, kb = wi.kb, ke = wi.ke;
   const int head0 = blockIdx.y * C::HG + wh * C::HW;  // this wave's first head
-
-  // Key range of this (row, split).
-  int L = seq_lens[b];
-  L = max(0, min(L, max_blocks * BLOCK));
-  const int nvis = max(0, min(L, L - (q_len - 1 - m)));
-  const int nblk = (L + BLOCK - 1) / BLOCK;
-  const int cpb = (nblk + S - 1) / S;
-  const int kb = min(s * cpb * BLOCK, nvis);
-  const int ke = min((s + 1) * cpb * BLOCK, nvis);
-  // kb is block aligned unless the split is empty (kb == ke == nvis).
+  // kb is block aligned unless the range is empty or given unaligned by a plan
   const int t_begin = kb / C::TT, t_end = kb < ke ? (ke + C::TT - 1) / C::TT : t_begin;
 
   const char* cache_bytes = reinterpret_cast<const char*>(cache);
@@ -169,24 +160,27 @@ __global__ void __launch_bounds__(C::THREADS, 1) decode_kernel(
   for (int t = t_begin; t < t_end; ++t) {
     char* st = smem + ((t - t_begin) & 1) * C::STAGE;
     const long blk = blk_next;
-    __builtin_amdgcn_s_waitcnt(0xF70);  // this wave's loads of tile t have landed
-    __syncthreads();                    // everyone's loads landed, tile t-1 is consumed
+    tile_barrier();  // everyone's loads of tile t landed, tile t-1 is consumed
     if (t + 1 < t_end) {
       blk_next = tile_block(t + 1);
       if (blk_next >= 0)
         issue_tile<E, C>(smem + ((t + 1 - t_begin) & 1) * C::STAGE, cache_bytes, blk_next,
                          ((t + 1) * C::TT) % BLOCK, wave);
     }
-    const int nv = blk < 0 ? 0 : min(C::TT, ke - t * C::TT);  // valid rows of this tile
-    if (nv <= 0) continue;
-    if (nv < C::TT) {
-      // Rows past the sequence end hold undefined data: zero them so that
-      // P = 0 times the row stays 0.
-      for (int e = threadIdx.x; e < (C::TT - nv) * (C::ROWB / 16); e += C::THREADS) {
-        const int r = nv + e / (C::ROWB / 16), q = e % (C::ROWB / 16);
+    // valid rows [lo, nv) of this tile; a missing block contributes nothing
+    const int lo = max(0, kb - t * C::TT);
+    const int nv = blk < 0 ? 0 : min(C::TT, ke - t * C::TT);
+    if (nv <= lo) continue;
+    if (lo > 0 || nv < C::TT) {
+      // Rows outside the range hold other keys or undefined data: zero them so
+      // that P = 0 times the row stays 0.
+      const int nz = C::TT - (nv - lo);
+      for (int e = threadIdx.x; e < nz * (C::ROWB / 16); e += C::THREADS) {
+        const int z = e / (C::ROWB / 16), q = e % (C::ROWB / 16);
+        const int r = z < lo ? z : nv + (z - lo);
         *reinterpret_cast<uint4*>(st + r * C::RS + q * 16) = uint4{0, 0, 0, 0};
       }
-      __syncthreads();
+      lds_barrier();
     }
 
 #pragma unroll
@@ -230,7 +224,7 @@ __global__ void __launch_bounds__(C::THREADS, 1) decode_kernel(
           for (int i = 0; i < 4; ++i) {
             const int row = rb + tb * 16 + 4 * g + i;
             float v = sc[hb][tb][i] * scale_log2;
-            v = (tb < C::CTB && row < nv) ? v : -INFINITY;
+            v = (tb < C::CTB && row >= lo && row < nv) ? v : -INFINITY;
             p[hb][tb][i] = v;
             mx = fmaxf(mx, v);
           }
@@ -276,9 +270,8 @@ __global__ void __launch_bounds__(C::THREADS, 1) decode_kernel(
   }
 
   // ---- epilogue ------------------------------------------------------------
-  const long orow = (S == 1) ? (long)(b * q_len + m) : ((long)(b * S + s) * q_len + m);
-  float* obase = o_out + orow * n_h * D_C;
-  float* lbase = lse_out + orow * n_h;
+  float* obase = (wi.part ? o_part : o_lat) + wi.orow * n_h * D_C;
+  float* lbase = (wi.part ? lse_part : lse) + wi.orow * n_h;
   if constexpr (C::NWT == 1) {
 #pragma unroll
     for (int hb = 0; hb < C::HB; ++hb) {
@@ -339,48 +332,44 @@ __global__ void __launch_bounds__(C::THREADS, 1) decode_kernel(
 template <class E, class C>
 hipError_t launch(const void* q_lat, const void* cache, int num_blocks, const int* table,
                   int max_blocks, const int* seq_lens, int B, int q_len, int n_h, float scale,
-                  int S, float* o_out, float* lse_out, hipStream_t stream) {
-  dim3 grid((unsigned)B * q_len * S, n_h / C::HG), block(C::THREADS);
+                  int S, const int* work, int n_work, float* o_lat, float* lse, float* o_part,
+                  float* lse_part, hipStream_t stream) {
+  const long n_items = work != nullptr ? (long)n_work : (long)B * q_len * S;
+  if (n_items == 0) return hipSuccess;
+  dim3 grid((unsigned)n_items, n_h / C::HG), block(C::THREADS);
   using T = typename E::storage;
   hipLaunchKernelGGL((decode_kernel<E, C>), grid, block, 0, stream, (const T*)q_lat,
                      (const T*)cache, num_blocks, table, max_blocks, seq_lens, q_len, n_h,
-                     scale * LOG2E, S, o_out, lse_out);
+                     B * q_len, scale * LOG2E, S, (const int4*)work, o_lat, lse, o_part,
+                     lse_part);
   return hipGetLastError();
 }
+
+#define MLA_DECODE_ARGS q_lat, cache, num_blocks, table, max_blocks, seq_lens, B, q_len, n_h, \
+                        scale, S, work, n_work, o_lat, lse, o_part, lse_part, stream
 
 template <class E, int TT>
 hipError_t dispatch_heads(const void* q_lat, const void* cache, int num_blocks, const int* table,
                           int max_blocks, const int* seq_lens, int B, int q_len, int n_h,
-                          float scale, int S, float* o_out, float* lse_out, hipStream_t stream) {
+                          float scale, int S, const int* work, int n_work, float* o_lat,
+                          float* lse, float* o_part, float* lse_part, hipStream_t stream) {
   constexpr int NWT16 = TT / 16 < 4 ? TT / 16 : 4;   // token slices for a lone head block
-  if (n_h == 16)
-    return launch<E, Cfg<E, 16, 1, NWT16, TT>>(q_lat, cache, num_blocks, table, max_blocks,
-                                               seq_lens, B, q_len, n_h, scale, S, o_out,
-                                               lse_out, stream);
-  if (n_h == 32)
-    return launch<E, Cfg<E, 16, 2, 2, TT>>(q_lat, cache, num_blocks, table, max_blocks, seq_lens,
-                                           B, q_len, n_h, scale, S, o_out, lse_out, stream);
-  if constexpr (std::is_same<E, BF16>::value) {
-    if (n_h % 128 == 0)
-      return launch<E, Cfg<E, 32, 4, 1, TT>>(q_lat, cache, num_blocks, table, max_blocks,
-                                             seq_lens, B, q_len, n_h, scale, S, o_out, lse_out,
-                                             stream);
-  }
-  return launch<E, Cfg<E, 16, 4, 1, TT>>(q_lat, cache, num_blocks, table, max_blocks, seq_lens, B,
-                                         q_len, n_h, scale, S, o_out, lse_out, stream);
+  if (n_h == 16) return launch<E, Cfg<E, 16, 1, NWT16, TT>>(MLA_DECODE_ARGS);
+  if (n_h == 32) return launch<E, Cfg<E, 16, 2, 2, TT>>(MLA_DECODE_ARGS);
+  return launch<E, Cfg<E, 16, 4, 1, TT>>(MLA_DECODE_ARGS);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const void* q_lat, const void* cache, int num_blocks, const int* table,
                          int max_blocks, const int* seq_lens, int B, int q_len, int n_h,
-                         int dtype, float scale, int num_splits, float* o_out, float* lse_out,
+                         int dtype, float scale, int S, const int* work, int n_work,
+                         float* o_lat, float* lse, float* o_part, float* lse_part,
                          hipStream_t stream) {
-  if (dtype == 1)
-    return dispatch_heads<BF16, 64>(q_lat, cache, num_blocks, table, max_blocks, seq_lens, B,
-                                    q_len, n_h, scale, num_splits, o_out, lse_out, stream);
-  return dispatch_heads<F32, 32>(q_lat, cache, num_blocks, table, max_blocks, seq_lens, B, q_len,
-                                 n_h, scale, num_splits, o_out, lse_out, stream);
+  if (dtype == 1 && n_h % 64 == 0)
+    return launch_decode_h64(MLA_DECODE_ARGS);
+  if (dtype == 1) return dispatch_heads<BF16, 64>(MLA_DECODE_ARGS);
+  return dispatch_heads<F32, 32>(MLA_DECODE_ARGS);
 }
 
 }  // namespace mla

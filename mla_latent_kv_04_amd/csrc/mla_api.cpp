@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "../../include/mla.h"
 #include "mla_internal.h"
 
@@ -15,9 +18,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool dtype_ok(int32_t dt) { return dt == MLA_F32 || dt == MLA_BF16; }
 
 // Head counts the decode kernels are built for.
-bool decode_heads_ok(int32_t n_h) {
-  return n_h == 16 || n_h == 32 || n_h == 64 || (n_h > 0 && n_h % 128 == 0);
-}
+bool decode_heads_ok(int32_t n_h) { return n_h == 16 || n_h == 32 || (n_h > 0 && n_h % 64 == 0); }
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
@@ -94,7 +95,107 @@ int32_t mla_decode_paged(const void* q_lat, const void* kv_cache, int32_t num_bl
     return MLA_ERR_ALIGN;
   return hip_status(mla::launch_decode(q_lat, kv_cache, num_blocks, block_table, max_blocks,
                                        seq_lens, B, q_len, n_h, dtype, softmax_scale, num_splits,
-                                       o_out, l_out, (hipStream_t)stream));
+                                       nullptr, 0, o_lat, lse, o_part, lse_part,
+                                       (hipStream_t)stream));
+}
+
+int32_t mla_plan_decode(const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t block_size,
+                        int32_t n_h, int32_t num_slots, int32_t max_work, int32_t* work,
+                        int32_t* n_work, int32_t* split, int32_t* n_split, int32_t* n_parts) {
+  if (B < 0 || q_len < 1 || block_size != MLA_BLOCK || n_h < 1 || num_slots < 1 || max_work < 0)
+    return MLA_ERR_SHAPE;
+  if (!n_work || !n_split || !n_parts) return MLA_ERR_NULL;
+  if (B > 0 && !seq_lens) return MLA_ERR_NULL;
+  const int64_t rows = (int64_t)B * q_len;
+  if (rows > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  std::vector<int64_t> nkeys(rows), tiles(rows), pieces(rows);
+  int64_t total = 0;
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t L = std::max<int64_t>(0, seq_lens[r / q_len]);
+    const int64_t m = r % q_len;
+    nkeys[r] = std::max<int64_t>(0, std::min<int64_t>(L, L - (q_len - 1 - m)));
+    tiles[r] = (nkeys[r] + block_size - 1) / block_size;
+    total += tiles[r];
+  }
+  const int64_t groups = (n_h % 64 == 0) ? n_h / 64 : 1;
+  const int64_t W = std::max<int64_t>(1, (groups * total + num_slots - 1) / num_slots);
+  int64_t count = 0, nsplit = 0, parts = 0;
+  for (int64_t r = 0; r < rows; ++r) {
+    pieces[r] = std::max<int64_t>(1, (tiles[r] + W - 1) / W);
+    count += pieces[r];
+    if (pieces[r] > 1) { ++nsplit; parts += pieces[r]; }
+  }
+  if (count > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  *n_work = (int32_t)count;
+  *n_split = (int32_t)nsplit;
+  *n_parts = (int32_t)parts;
+  if (count > max_work || nsplit > max_work) return MLA_ERR_SHAPE;
+  if (count > 0 && !work) return MLA_ERR_NULL;
+  if (nsplit > 0 && !split) return MLA_ERR_NULL;
+  struct Piece { int64_t blocks, row, k, kb, ke, slot; };
+  std::vector<Piece> items;
+  items.reserve(count);
+  int64_t slot = 0, si = 0;
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t T = tiles[r], P = pieces[r];
+    if (P > 1) {
+      split[si * 3] = (int32_t)r;
+      split[si * 3 + 1] = (int32_t)slot;
+      split[si * 3 + 2] = (int32_t)P;
+      ++si;
+    }
+    for (int64_t k = 0; k < P; ++k) {
+      const int64_t b0 = k * T / P, b1 = (k + 1) * T / P;
+      items.push_back({b1 - b0, r, k, b0 * block_size, std::min(b1 * block_size, nkeys[r]),
+                       P > 1 ? slot + k : -1});
+    }
+    if (P > 1) slot += P;
+  }
+  std::stable_sort(items.begin(), items.end(), [](const Piece& a, const Piece& b) {
+    if (a.blocks != b.blocks) return a.blocks > b.blocks;
+    if (a.row != b.row) return a.row < b.row;
+    return a.k < b.k;
+  });
+  for (int64_t i = 0; i < count; ++i) {
+    work[i * 4] = (int32_t)items[i].row;
+    work[i * 4 + 1] = (int32_t)items[i].kb;
+    work[i * 4 + 2] = (int32_t)items[i].ke;
+    work[i * 4 + 3] = (int32_t)items[i].slot;
+  }
+  return MLA_OK;
+}
+
+int32_t mla_decode_paged_planned(const void* q_lat, const void* kv_cache, int32_t num_blocks,
+                                 int32_t block_size, const int32_t* block_table,
+                                 int32_t max_blocks, int32_t B, int32_t q_len, int32_t n_h,
+                                 int32_t dtype, float softmax_scale, const int32_t* work,
+                                 int32_t n_work, float* o_part, float* lse_part, float* o_lat,
+                                 float* lse, void* stream) {
+  if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  if (B < 0 || q_len < 1 || num_blocks < 1 || max_blocks < 1 || block_size != MLA_BLOCK ||
+      !decode_heads_ok(n_h) || n_work < 0 || !(softmax_scale > 0.0f))
+    return MLA_ERR_SHAPE;
+  if ((int64_t)B * q_len > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  if (n_work == 0 || B == 0) return MLA_OK;
+  if (!q_lat || !kv_cache || !block_table || !work || !o_lat || !lse) return MLA_ERR_NULL;
+  if (!aligned16(q_lat) || !aligned16(kv_cache) || !aligned16(o_lat) || !aligned4(lse) ||
+      !aligned16(work) || (o_part && !aligned16(o_part)) || (lse_part && !aligned4(lse_part)))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_decode(q_lat, kv_cache, num_blocks, block_table, max_blocks,
+                                       nullptr, B, q_len, n_h, dtype, softmax_scale, 1, work,
+                                       n_work, o_lat, lse, o_part, lse_part,
+                                       (hipStream_t)stream));
+}
+
+int32_t mla_combine_planned(const float* o_part, const float* lse_part, const int32_t* split,
+                            int32_t n_split, int32_t n_h, float* o_lat, float* lse, void* stream) {
+  if (n_split < 0 || n_h < 1) return MLA_ERR_SHAPE;
+  if (n_split == 0) return MLA_OK;
+  if (!o_part || !lse_part || !split || !o_lat) return MLA_ERR_NULL;
+  if (!aligned16(o_part) || !aligned16(o_lat) || !aligned4(lse_part) || (lse && !aligned4(lse)))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_combine_planned(o_part, lse_part, split, n_split, n_h, o_lat, lse,
+                                                (hipStream_t)stream));
 }
 
 int32_t mla_splitkv_combine(const float* o_part, const float* lse_part, int32_t B, int32_t S,

@@ -126,12 +126,74 @@ __device__ __forceinline__ float group4_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() carries a memory
+// fence, and the compiler then waits for every outstanding global load first,
+// including direct global->LDS loads of the next tile that are meant to stay
+// in flight.  Here only this wave's LDS operations are waited for.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");       // keep LDS accesses on their side of the barrier
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait for this wave's vector-memory loads (the tile's direct-to-LDS loads),
+// then a full workgroup barrier.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0)
+  __syncthreads();
+}
+
 // RoPE pair k at position pos: cos/sin of pos * base^(-2k/64), with the angle
 // formed and evaluated in float64 (fp32 angles lose ~1e-2 rad near 128K).
 __device__ __forceinline__ void rope_cs(int pos, int k, double base, double& c, double& s) {
   double theta = pow(base, -(double)(2 * k) / (double)D_R);
   double ang = (double)pos * theta;
   sincos(ang, &s, &c);
+}
+
+// One unit of attention work: query row (b, m) against keys [kb, ke) of
+// sequence b, written to row `orow` of o_lat (part == false) or of the split
+// partials (part == true).
+struct WorkItem {
+  int b, m, kb, ke;
+  long orow;
+  bool part;
+  bool valid;
+};
+
+// Uniform split-KV (work == nullptr): item = (b * q_len + m) * S + s, split s of
+// sequence b's blocks cut into S runs of ceil(nblk / S) blocks.  Planned
+// (work != nullptr): work[item] = {row, key_begin, key_end, slot}.
+__device__ __forceinline__ WorkItem decode_item(int item, const int4* work, int n_rows, int q_len,
+                                                int S, const int* seq_lens, int max_blocks) {
+  WorkItem w;
+  const int cap = max_blocks * BLOCK;
+  if (work != nullptr) {
+    const int4 v = work[item];
+    w.valid = v.x >= 0 && v.x < n_rows;
+    const int row = w.valid ? v.x : 0;
+    w.b = row / q_len;
+    w.m = row % q_len;
+    w.kb = max(0, min(v.y, cap));
+    w.ke = max(w.kb, min(v.z, cap));
+    w.part = v.w >= 0;
+    w.orow = w.part ? (long)v.w : (long)row;
+    return w;
+  }
+  const int s = item % S, bm = item / S;
+  w.valid = true;
+  w.m = bm % q_len;
+  w.b = bm / q_len;
+  const int L = max(0, min(seq_lens[w.b], cap));
+  const int nvis = max(0, min(L, L - (q_len - 1 - w.m)));
+  const int nblk = (L + BLOCK - 1) / BLOCK;
+  const int cpb = (nblk + S - 1) / S;
+  w.kb = min(s * cpb * BLOCK, nvis);
+  w.ke = min((s + 1) * cpb * BLOCK, nvis);
+  w.part = S > 1;
+  w.orow = w.part ? ((long)(w.b * S + s) * q_len + w.m) : (long)(w.b * q_len + w.m);
+  return w;
 }
 
 }  // namespace mla

@@ -29,7 +29,12 @@ def _to_device(x: np.ndarray, dtype, device):
 
 @dataclasses.dataclass
 class DeviceProblem:
-    """Device-resident inputs, cache and work buffers of one workload."""
+    """Device-resident inputs, cache and work buffers of one workload.
+
+    num_splits > 0: uniform split-KV with that many splits per row.
+    num_splits == 0: a load-balanced work list from mla_plan_decode (``work``,
+    ``split``) sized for ``num_slots`` concurrent workgroups.
+    """
     prob: Problem
     num_splits: int
     dtype: object
@@ -51,6 +56,9 @@ class DeviceProblem:
     o_lat: object
     lse: object
     out: object
+    work: Optional[object] = None
+    split: Optional[object] = None
+    n_parts: int = 0
 
     @property
     def B(self):
@@ -77,10 +85,18 @@ def new_rows(prob: Problem):
     return np.array(seqs, dtype=np.int64), np.array(poss, dtype=np.int64)
 
 
+def device_slots(device="cuda") -> int:
+    """Workgroups the attention kernels run at once: one per compute unit."""
+    torch = _torch()
+    return int(torch.cuda.get_device_properties(torch.device(device)).multi_processor_count)
+
+
 def upload(prob: Problem, num_splits: Optional[int] = None, device="cuda",
-           poison: bool = True) -> DeviceProblem:
+           poison: bool = True, num_slots: Optional[int] = None) -> DeviceProblem:
     """Copy a generated problem to the GPU and fill the cache with every row the
-    step does not append itself (with the library's own append kernel)."""
+    step does not append itself (with the library's own append kernel).
+
+    num_splits None -> the workload's own; 0 -> a balanced work plan."""
     torch = _torch()
     wl = prob.wl
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -107,6 +123,14 @@ def upload(prob: Problem, num_splits: Optional[int] = None, device="cuda",
                           ROPE_BASE)
     new_idx = prob.key_offsets[step_seq] + step_pos
     T = prob.T
+    work = split = None
+    n_parts = 0
+    if S == 0:
+        slots = device_slots(device) if num_slots is None else int(num_slots)
+        w, sp, n_parts = mla.mla_plan_decode(prob.seq_lens, wl.q_len, wl.n_h, slots)
+        work = torch.from_numpy(w).to(device)
+        split = torch.from_numpy(sp).to(device)
+    n_part_rows = n_parts if S == 0 else (wl.B * S * wl.q_len if S > 1 else 0)
     dp = DeviceProblem(
         prob=prob, num_splits=S, dtype=dt, kv_cache=kv_cache, block_table=block_table,
         seq_lens=seq_lens,
@@ -118,13 +142,14 @@ def upload(prob: Problem, num_splits: Optional[int] = None, device="cuda",
         q_pos=torch.from_numpy(prob.q_pos).to(device),
         w_uk=_to_device(prob.w_uk, dt, device), w_uv=_to_device(prob.w_uv, dt, device),
         q_lat=torch.empty((T, wl.n_h, ROW), dtype=dt, device=device),
-        o_part=(torch.empty((wl.B, S, wl.q_len, wl.n_h, D_C), dtype=torch.float32, device=device)
-                if S > 1 else None),
-        lse_part=(torch.empty((wl.B, S, wl.q_len, wl.n_h), dtype=torch.float32, device=device)
-                  if S > 1 else None),
+        o_part=(torch.empty((n_part_rows, wl.n_h, D_C), dtype=torch.float32, device=device)
+                if n_part_rows else None),
+        lse_part=(torch.empty((n_part_rows, wl.n_h), dtype=torch.float32, device=device)
+                  if n_part_rows else None),
         o_lat=torch.empty((T, wl.n_h, D_C), dtype=torch.float32, device=device),
         lse=torch.empty((T, wl.n_h), dtype=torch.float32, device=device),
         out=torch.empty((T, wl.n_h, D_H), dtype=torch.float32, device=device),
+        work=work, split=split, n_parts=n_parts,
     )
     return dp
 
@@ -141,7 +166,14 @@ def step(dp: DeviceProblem, stream=None):
 def decode(dp: DeviceProblem, stream=None):
     """Attention over the cache (+ split merge) into dp.o_lat / dp.lse."""
     S = dp.num_splits
-    if S > 1:
+    if S == 0:
+        mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
+                                     softmax_scale(), dp.work, dp.o_lat, dp.lse,
+                                     o_part=dp.o_part, lse_part=dp.lse_part, stream=stream)
+        if dp.split.shape[0] > 0:
+            mla.mla_combine_planned(dp.o_part, dp.lse_part, dp.split, dp.n_h, dp.o_lat, dp.lse,
+                                    stream=stream)
+    elif S > 1:
         mla.mla_decode_paged(dp.q_lat, dp.kv_cache, dp.block_table, dp.seq_lens, dp.q_len,
                              softmax_scale(), S, o_part=dp.o_part, lse_part=dp.lse_part,
                              stream=stream)

@@ -57,22 +57,23 @@ class Workload:
     block_size: int = BLOCK
     table: str = "permuted"   # "identity" or "permuted"
     seed: int = 0
-    num_splits: int = 1       # split-KV partitions of the benchmark's launch
+    num_splits: int = 0       # split-KV partitions of the benchmark's launch (0 = balanced plan)
 
 
 # The five workloads: V2-Lite fp32 (tiny), V2-Lite bf16 paged, full V2 ragged
 # decode, V2 128K split-KV decode and V2 chunked prefill.
 WORKLOADS = {
     "v2lite_f32_L256": Workload("v2lite_f32_L256", "f32", B=1, n_h=16, ctx=256,
-                                table="identity", seed=1001),
+                                table="identity", seed=1001, num_splits=1),
     "v2lite_bf16_B64_L4096": Workload("v2lite_bf16_B64_L4096", "bf16", B=64, n_h=16,
-                                      ctx=4096, seed=1002, num_splits=4),
+                                      ctx=4096, seed=1002),
     "v2_bf16_B128_L1k-8k": Workload("v2_bf16_B128_L1k-8k", "bf16", B=128, n_h=128,
-                                    ctx=(1024, 8192), seed=1003, num_splits=2),
+                                    ctx=(1024, 8192), seed=1003),
     "v2_bf16_B4_L128k_splitkv": Workload("v2_bf16_B4_L128k_splitkv", "bf16", B=4, n_h=128,
-                                         ctx=131072, seed=1004, num_splits=64),
+                                         ctx=131072, seed=1004),
     "v2_bf16_prefill_6144+2048": Workload("v2_bf16_prefill_6144+2048", "bf16", B=1,
-                                          n_h=128, ctx=8192, q_len=2048, seed=1005),
+                                          n_h=128, ctx=8192, q_len=2048, seed=1005,
+                                          num_splits=1),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

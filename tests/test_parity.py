@@ -37,6 +37,12 @@ SMALL_CASES = [
     (F3, dict(B=2, ctx=[1030, 1500], n_h=256), 2),
     (F1, dict(B=2, ctx=150, n_h=32, q_len=5), 2),
     (F1, dict(B=2, ctx=100, n_h=128), 1),
+    # balanced work plans (num_splits 0)
+    (F3, dict(B=4, ctx=[1, 65, 2000, 129]), 0),
+    (F2, dict(B=3, ctx=[300, 4000, 64]), 0),
+    (F5, dict(ctx=1100, q_len=64), 0),
+    (F1, dict(B=3, ctx=[5, 700, 130]), 0),
+    (F3, dict(B=3, ctx=[0, 900, 3000], n_h=256), 0),
 ]
 
 
