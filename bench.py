@@ -29,7 +29,10 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MFMA_F32_PEAK_TFLOPS = 157.3
 
-DECODE_SOURCES = ["mla_latent_kv_04_amd/csrc/decode.hip", "mla_latent_kv_04_amd/csrc/mla_common.h"]
+# sources of the attention kernels; the committed HBM-traffic record is only
+# used while these are unchanged
+DECODE_SOURCES = ["mla_latent_kv_04_amd/csrc/decode.hip", "mla_latent_kv_04_amd/csrc/decode_h64.hip",
+                  "mla_latent_kv_04_amd/csrc/mla_common.h", "mla_latent_kv_04_amd/csrc/mla_api.cpp"]
 
 
 def log(*a):
@@ -127,6 +130,9 @@ def main():
                     help="split-KV partitions per row; 0 = balanced work plan (default: workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many bytes (a "
+                         "known-size reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -176,6 +182,16 @@ def main():
             mla.mla_splitkv_combine(dp.o_part, dp.lse_part, dp.B, splits, dp.q_len, dp.n_h,
                                     dp.o_lat, dp.lse)
         mla.mla_out_proj(dp.o_lat, dp.w_uv, dp.out)
+
+    if args.copy_bytes > 0:
+        n = args.copy_bytes // 4
+        src = torch.arange(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] reference copy of {4 * n} bytes done")
+        del src, dst
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -114,14 +114,21 @@ __device__ __forceinline__ float xor_shfl(float v, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(v)));
 }
 
-// Max / sum over the four lanes that share lane % 16 (lane groups 0..3).
+// Max / sum over the four lanes that share lane % 16 (lanes l, l^16, l^32,
+// l^48), without going through LDS: with both operands the same register,
+// v_permlane16_swap leaves lane l holding its own value and that of lane l^16
+// (one in each result), and v_permlane32_swap does the same for lane l^32.
 __device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, xor_shfl(v, 16));
-  return fmaxf(v, xor_shfl(v, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float group4_sum(float v) {
-  v += xor_shfl(v, 16);
-  return v + xor_shfl(v, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
