@@ -165,7 +165,7 @@ def main():
         if splits == 0:
             mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
                                          scale, dp.work, dp.o_lat, dp.lse, o_part=dp.o_part,
-                                         lse_part=dp.lse_part)
+                                         lse_part=dp.lse_part, lists=dp.lists)
         elif splits > 1:
             mla.mla_decode_paged(dp.q_lat, dp.kv_cache, dp.block_table, dp.seq_lens, dp.q_len,
                                  scale, splits, o_part=dp.o_part, lse_part=dp.lse_part)

@@ -200,45 +200,56 @@ int32_t mla_split_plan(const int32_t* seq_lens, int32_t B, int32_t block_size, i
                        int32_t* begin_end);
 
 /*
- * mla_plan_decode - a load-balanced split-KV work list, on the host.
+ * mla_plan_decode - a load-balanced split-KV schedule, on the host.
  *
  * Rows r = b * q_len + m; row r sees n_r keys (the visibility rule of
  * mla_decode_paged, with seq_lens[b] clamped at 0) and spans T_r = ceil(n_r / 64)
- * blocks.  With G = n_h / 64 workgroups per row piece when n_h is a multiple
- * of 64 (else G = 1) and W = max(1, ceil(G * sum_r T_r / num_slots)) blocks per
- * piece, row r is cut into P_r = max(1, ceil(T_r / W)) pieces; piece k covers
- * blocks [floor(k T_r / P_r), floor((k+1) T_r / P_r)), i.e. keys
- * [64 floor(k T_r / P_r), min(64 floor((k+1) T_r / P_r), n_r)).
- * Rows with one piece are written straight to o_lat; the pieces of a split
- * row get consecutive partial slots (rows in increasing order).
+ * blocks.  Lay the rows' blocks end to end (row 0 first): row r occupies
+ * positions [S_r, S_r + T_r) of a sequence of N = sum_r T_r blocks.  With
+ * G = n_h / 64 workgroups per unit of work when n_h is a multiple of 64 (else
+ * G = 1), K = max(1, min(floor(num_slots / G), N)) lists (K = 1 when N = 0),
+ * list k owns positions [floor(k N / K), floor((k+1) N / K)): equal shares to
+ * within one block, so that K * G workgroups finish together.  A row whose
+ * blocks fall in lists k0..k1 is cut at the list boundaries into k1 - k0 + 1
+ * segments; a row with no block is one empty segment in the list owning
+ * position S_r (the last list if S_r = N).  Segment keys are
+ * [64 t0, min(64 t1, n_r)) for its blocks [t0, t1) of the row.
  *
  *   work  (host out, int32 [n_work, 4]) = {row, key_begin, key_end, slot},
- *         slot = -1 for an unsplit row; items sorted by decreasing piece size
- *         (blocks), then row, then piece index, so the longest start first.
+ *         ordered by list, then row; slot = -1 for a row in one segment (its
+ *         output goes straight to o_lat), else the segments of a cut row get
+ *         consecutive partial slots (cut rows in increasing row order).
+ *   lists (host out, int32 [n_lists + 1], at most num_slots + 1 entries):
+ *         list k is work items lists[k] .. lists[k+1] - 1; lists[n_lists] = n_work.
  *   split (host out, int32 [n_split, 3]) = {row, first_slot, count} for every
- *         split row, in row order; n_parts = number of partial slots.
- * max_work bounds both arrays; if the plan needs more, MLA_ERR_SHAPE is
+ *         cut row, in row order; n_parts = number of partial slots.
+ * max_work bounds work and split; if the plan needs more, MLA_ERR_SHAPE is
  * returned and *n_work holds the required size.  num_slots: workgroups the
  * device runs at once (e.g. its compute-unit count).  Pure integer host code.
  */
 int32_t mla_plan_decode(const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t block_size,
                         int32_t n_h, int32_t num_slots, int32_t max_work, int32_t* work,
-                        int32_t* n_work, int32_t* split, int32_t* n_split, int32_t* n_parts);
+                        int32_t* n_work, int32_t* lists, int32_t* n_lists, int32_t* split,
+                        int32_t* n_split, int32_t* n_parts);
 
 /*
- * mla_decode_paged_planned - mla_decode_paged over a work list from
- * mla_plan_decode (copied to the device).  Item i scores its row's query
- * against keys [key_begin, key_end) of the row's sequence (b = row / q_len)
- * and writes o_lat/lse row `row` when slot < 0, else o_part/lse_part row
- * `slot` (fp32 [n_parts, n_h, 512] / [n_parts, n_h]).  Arguments as in
+ * mla_decode_paged_planned - mla_decode_paged over a schedule from
+ * mla_plan_decode (work and lists copied to the device).  Item i scores its
+ * row's query against keys [key_begin, key_end) of the row's sequence
+ * (b = row / q_len) and writes o_lat/lse row `row` when slot < 0, else
+ * o_part/lse_part row `slot` (fp32 [n_parts, n_h, 512] / [n_parts, n_h]).
+ * lists (device int32 [n_lists + 1], may be NULL): the items of each list are
+ * run in order by one workgroup per 64 heads; results do not depend on it
+ * (NULL runs one item per workgroup).  Other arguments as in
  * mla_decode_paged; key ranges are clamped to max_blocks * 64.
  */
 int32_t mla_decode_paged_planned(const void* q_lat, const void* kv_cache, int32_t num_blocks,
                                  int32_t block_size, const int32_t* block_table,
                                  int32_t max_blocks, int32_t B, int32_t q_len, int32_t n_h,
                                  int32_t dtype, float softmax_scale, const int32_t* work,
-                                 int32_t n_work, float* o_part, float* lse_part, float* o_lat,
-                                 float* lse, void* stream);
+                                 int32_t n_work, const int32_t* lists, int32_t n_lists,
+                                 float* o_part, float* lse_part, float* o_lat, float* lse,
+                                 void* stream);
 
 /*
  * mla_combine_planned - merge the partials of every split row of a plan

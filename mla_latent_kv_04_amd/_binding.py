@@ -59,9 +59,9 @@ def load() -> ctypes.CDLL:
         "mla_splitkv_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
         "mla_out_proj": (_I, [_P, _P, _I, _I, _I, _P, _P]),
         "mla_split_plan": (_I, [_P, _I, _I, _I, _P]),
-        "mla_plan_decode": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+        "mla_plan_decode": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
         "mla_decode_paged_planned": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _F, _P, _I,
-                                          _P, _P, _P, _P, _P]),
+                                          _P, _I, _P, _P, _P, _P, _P]),
         "mla_combine_planned": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
@@ -247,10 +247,13 @@ def mla_split_plan(seq_lens, num_splits, block_size=BLOCK) -> np.ndarray:
 
 
 def mla_plan_decode(seq_lens, q_len, n_h, num_slots, block_size=BLOCK):
-    """Host work plan (see mla.h).  Returns (work int32 [n, 4], split int32 [k, 3], n_parts)."""
+    """Host schedule (see mla.h).  Returns (work int32 [n, 4], lists int32 [K + 1],
+    split int32 [k, 3], n_parts)."""
     sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
     B = int(sl.shape[0])
-    n_work, n_split, n_parts = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    n_work, n_lists = ctypes.c_int32(0), ctypes.c_int32(0)
+    n_split, n_parts = ctypes.c_int32(0), ctypes.c_int32(0)
+    lists = np.zeros(max(1, int(num_slots)) + 1, dtype=np.int32)
     cap = 16
     while True:
         work = np.zeros((cap, 4), dtype=np.int32)
@@ -258,10 +261,12 @@ def mla_plan_decode(seq_lens, q_len, n_h, num_slots, block_size=BLOCK):
         st = load().mla_plan_decode(sl.ctypes.data_as(ctypes.c_void_p), B, int(q_len),
                                     int(block_size), int(n_h), int(num_slots), cap,
                                     work.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n_work),
+                                    lists.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n_lists),
                                     split.ctypes.data_as(ctypes.c_void_p), ctypes.byref(n_split),
                                     ctypes.byref(n_parts))
         if st == MLA_OK:
-            return work[:n_work.value].copy(), split[:n_split.value].copy(), int(n_parts.value)
+            return (work[:n_work.value].copy(), lists[:n_lists.value + 1].copy(),
+                    split[:n_split.value].copy(), int(n_parts.value))
         if st == 2 and max(n_work.value, n_split.value) > cap:
             cap = max(n_work.value, n_split.value)
             continue
@@ -269,8 +274,9 @@ def mla_plan_decode(seq_lens, q_len, n_h, num_slots, block_size=BLOCK):
 
 
 def mla_decode_paged_planned(q_lat, kv_cache, block_table, B, q_len, softmax_scale, work,
-                             o_lat, lse, o_part=None, lse_part=None, stream=None):
-    """Attention over a device work list from mla_plan_decode (see mla.h)."""
+                             o_lat, lse, o_part=None, lse_part=None, lists=None, stream=None):
+    """Attention over a device schedule from mla_plan_decode (see mla.h); lists
+    (device int32 [K + 1]) is optional."""
     torch = _torch()
     dt = _dtype_code(q_lat)
     if kv_cache.dtype != q_lat.dtype:
@@ -281,6 +287,8 @@ def mla_decode_paged_planned(q_lat, kv_cache, block_table, B, q_len, softmax_sca
         raise ValueError("q_lat must hold [B, q_len, n_h, 576]")
     if work.dim() != 2 or work.shape[1] != 4:
         raise ValueError("work must be [n_work, 4]")
+    if lists is not None and (lists.dim() != 1 or lists.shape[0] < 2):
+        raise ValueError("lists must be [n_lists + 1]")
     if o_lat.numel() != rows * n_h * D_C or lse.numel() != rows * n_h:
         raise ValueError("o_lat / lse must hold [B, q_len, n_h, 512] / [B, q_len, n_h]")
     if o_part is not None and (o_part.shape[-1] != D_C or o_part.numel() % (n_h * D_C) or
@@ -291,7 +299,8 @@ def mla_decode_paged_planned(q_lat, kv_cache, block_table, B, q_len, softmax_sca
         _dev(q_lat, "q_lat"), _dev(kv_cache, "kv_cache"), int(kv_cache.shape[0]),
         int(kv_cache.shape[1]), _dev(block_table, "block_table", torch.int32),
         int(block_table.shape[1]), int(B), int(q_len), n_h, dt, float(softmax_scale),
-        _dev(work, "work", torch.int32), int(work.shape[0]), _dev(o_part, "o_part", f32),
+        _dev(work, "work", torch.int32), int(work.shape[0]), _dev(lists, "lists", torch.int32),
+        int(lists.shape[0]) - 1 if lists is not None else 0, _dev(o_part, "o_part", f32),
         _dev(lse_part, "lse_part", f32), _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32),
         _stream(stream))
     _check("mla_decode_paged_planned", st)

@@ -364,10 +364,12 @@ hipError_t dispatch_heads(const void* q_lat, const void* cache, int num_blocks, 
 hipError_t launch_decode(const void* q_lat, const void* cache, int num_blocks, const int* table,
                          int max_blocks, const int* seq_lens, int B, int q_len, int n_h,
                          int dtype, float scale, int S, const int* work, int n_work,
-                         float* o_lat, float* lse, float* o_part, float* lse_part,
-                         hipStream_t stream) {
+                         const int* lists, int n_lists, float* o_lat, float* lse, float* o_part,
+                         float* lse_part, hipStream_t stream) {
   if (dtype == 1 && n_h % 64 == 0)
-    return launch_decode_h64(MLA_DECODE_ARGS);
+    return launch_decode_h64(q_lat, cache, num_blocks, table, max_blocks, seq_lens, B, q_len,
+                             n_h, scale, S, work, n_work, lists, n_lists, o_lat, lse, o_part,
+                             lse_part, stream);
   if (dtype == 1) return dispatch_heads<BF16, 64>(MLA_DECODE_ARGS);
   return dispatch_heads<F32, 32>(MLA_DECODE_ARGS);
 }

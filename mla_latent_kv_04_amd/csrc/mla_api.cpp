@@ -95,73 +95,88 @@ int32_t mla_decode_paged(const void* q_lat, const void* kv_cache, int32_t num_bl
     return MLA_ERR_ALIGN;
   return hip_status(mla::launch_decode(q_lat, kv_cache, num_blocks, block_table, max_blocks,
                                        seq_lens, B, q_len, n_h, dtype, softmax_scale, num_splits,
-                                       nullptr, 0, o_lat, lse, o_part, lse_part,
+                                       nullptr, 0, nullptr, 0, o_lat, lse, o_part, lse_part,
                                        (hipStream_t)stream));
 }
 
 int32_t mla_plan_decode(const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t block_size,
                         int32_t n_h, int32_t num_slots, int32_t max_work, int32_t* work,
-                        int32_t* n_work, int32_t* split, int32_t* n_split, int32_t* n_parts) {
+                        int32_t* n_work, int32_t* lists, int32_t* n_lists, int32_t* split,
+                        int32_t* n_split, int32_t* n_parts) {
   if (B < 0 || q_len < 1 || block_size != MLA_BLOCK || n_h < 1 || num_slots < 1 || max_work < 0)
     return MLA_ERR_SHAPE;
-  if (!n_work || !n_split || !n_parts) return MLA_ERR_NULL;
+  if (!n_work || !n_lists || !n_split || !n_parts) return MLA_ERR_NULL;
   if (B > 0 && !seq_lens) return MLA_ERR_NULL;
   const int64_t rows = (int64_t)B * q_len;
   if (rows > 0x7fffffffLL) return MLA_ERR_SHAPE;
-  std::vector<int64_t> nkeys(rows), tiles(rows), pieces(rows);
+  // visible keys and blocks per row, and each row's first position in the
+  // concatenation of all rows' blocks
+  std::vector<int64_t> nkeys(rows), tiles(rows), start(rows);
   int64_t total = 0;
   for (int64_t r = 0; r < rows; ++r) {
     const int64_t L = std::max<int64_t>(0, seq_lens[r / q_len]);
     const int64_t m = r % q_len;
     nkeys[r] = std::max<int64_t>(0, std::min<int64_t>(L, L - (q_len - 1 - m)));
     tiles[r] = (nkeys[r] + block_size - 1) / block_size;
+    start[r] = total;
     total += tiles[r];
   }
   const int64_t groups = (n_h % 64 == 0) ? n_h / 64 : 1;
-  const int64_t W = std::max<int64_t>(1, (groups * total + num_slots - 1) / num_slots);
-  int64_t count = 0, nsplit = 0, parts = 0;
+  const int64_t K = total > 0 ? std::max<int64_t>(1, std::min<int64_t>(num_slots / groups, total)) : 1;
+  // list k covers concatenated blocks [bound(k), bound(k + 1))
+  auto bound = [&](int64_t k) { return k * total / K; };
+  auto list_of = [&](int64_t pos) {  // the list whose range holds block pos (pos < total)
+    int64_t k = pos * K / std::max<int64_t>(total, 1);
+    while (k + 1 < K && bound(k + 1) <= pos) ++k;
+    while (k > 0 && bound(k) > pos) --k;
+    return k;
+  };
+  struct Seg { int64_t list, row, kb, ke, slot; };
+  std::vector<Seg> segs;
+  std::vector<int64_t> splits;   // {row, first slot, pieces} per split row, in row order
+  int64_t parts = 0;
   for (int64_t r = 0; r < rows; ++r) {
-    pieces[r] = std::max<int64_t>(1, (tiles[r] + W - 1) / W);
-    count += pieces[r];
-    if (pieces[r] > 1) { ++nsplit; parts += pieces[r]; }
+    if (tiles[r] == 0) {   // a row with no key still gets its (empty) output written
+      segs.push_back({std::min(K - 1, total > 0 && start[r] < total ? list_of(start[r]) : K - 1), r,
+                      0, 0, -1});
+      continue;
+    }
+    const int64_t k0 = list_of(start[r]), k1 = list_of(start[r] + tiles[r] - 1);
+    const int64_t P = k1 - k0 + 1;
+    if (P > 1) splits.insert(splits.end(), {r, parts, P});
+    for (int64_t k = k0; k <= k1; ++k) {
+      const int64_t t0 = std::max(bound(k), start[r]) - start[r];
+      const int64_t t1 = std::min(bound(k + 1), start[r] + tiles[r]) - start[r];
+      segs.push_back({k, r, t0 * block_size, std::min(t1 * block_size, nkeys[r]),
+                      P > 1 ? parts + (k - k0) : -1});
+    }
+    if (P > 1) parts += P;
   }
+  const int64_t count = (int64_t)segs.size(), nsplit = (int64_t)splits.size() / 3;
   if (count > 0x7fffffffLL) return MLA_ERR_SHAPE;
   *n_work = (int32_t)count;
+  *n_lists = (int32_t)K;
   *n_split = (int32_t)nsplit;
   *n_parts = (int32_t)parts;
   if (count > max_work || nsplit > max_work) return MLA_ERR_SHAPE;
   if (count > 0 && !work) return MLA_ERR_NULL;
+  if (!lists) return MLA_ERR_NULL;
   if (nsplit > 0 && !split) return MLA_ERR_NULL;
-  struct Piece { int64_t blocks, row, k, kb, ke, slot; };
-  std::vector<Piece> items;
-  items.reserve(count);
-  int64_t slot = 0, si = 0;
-  for (int64_t r = 0; r < rows; ++r) {
-    const int64_t T = tiles[r], P = pieces[r];
-    if (P > 1) {
-      split[si * 3] = (int32_t)r;
-      split[si * 3 + 1] = (int32_t)slot;
-      split[si * 3 + 2] = (int32_t)P;
-      ++si;
-    }
-    for (int64_t k = 0; k < P; ++k) {
-      const int64_t b0 = k * T / P, b1 = (k + 1) * T / P;
-      items.push_back({b1 - b0, r, k, b0 * block_size, std::min(b1 * block_size, nkeys[r]),
-                       P > 1 ? slot + k : -1});
-    }
-    if (P > 1) slot += P;
-  }
-  std::stable_sort(items.begin(), items.end(), [](const Piece& a, const Piece& b) {
-    if (a.blocks != b.blocks) return a.blocks > b.blocks;
-    if (a.row != b.row) return a.row < b.row;
-    return a.k < b.k;
+  // by list, then by row: a list's segments are consecutive rows
+  std::stable_sort(segs.begin(), segs.end(), [](const Seg& a, const Seg& b) {
+    if (a.list != b.list) return a.list < b.list;
+    return a.row < b.row;
   });
+  int64_t li = 0;
   for (int64_t i = 0; i < count; ++i) {
-    work[i * 4] = (int32_t)items[i].row;
-    work[i * 4 + 1] = (int32_t)items[i].kb;
-    work[i * 4 + 2] = (int32_t)items[i].ke;
-    work[i * 4 + 3] = (int32_t)items[i].slot;
+    while (li <= segs[i].list) lists[li++] = (int32_t)i;
+    work[i * 4] = (int32_t)segs[i].row;
+    work[i * 4 + 1] = (int32_t)segs[i].kb;
+    work[i * 4 + 2] = (int32_t)segs[i].ke;
+    work[i * 4 + 3] = (int32_t)segs[i].slot;
   }
+  while (li <= K) lists[li++] = (int32_t)count;
+  for (int64_t i = 0; i < 3 * nsplit; ++i) split[i] = (int32_t)splits[i];
   return MLA_OK;
 }
 
@@ -169,11 +184,13 @@ int32_t mla_decode_paged_planned(const void* q_lat, const void* kv_cache, int32_
                                  int32_t block_size, const int32_t* block_table,
                                  int32_t max_blocks, int32_t B, int32_t q_len, int32_t n_h,
                                  int32_t dtype, float softmax_scale, const int32_t* work,
-                                 int32_t n_work, float* o_part, float* lse_part, float* o_lat,
-                                 float* lse, void* stream) {
+                                 int32_t n_work, const int32_t* lists, int32_t n_lists,
+                                 float* o_part, float* lse_part, float* o_lat, float* lse,
+                                 void* stream) {
   if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
   if (B < 0 || q_len < 1 || num_blocks < 1 || max_blocks < 1 || block_size != MLA_BLOCK ||
-      !decode_heads_ok(n_h) || n_work < 0 || !(softmax_scale > 0.0f))
+      !decode_heads_ok(n_h) || n_work < 0 || !(softmax_scale > 0.0f) ||
+      (lists && n_lists < 1))
     return MLA_ERR_SHAPE;
   if ((int64_t)B * q_len > 0x7fffffffLL) return MLA_ERR_SHAPE;
   if (n_work == 0 || B == 0) return MLA_OK;
@@ -183,8 +200,8 @@ int32_t mla_decode_paged_planned(const void* q_lat, const void* kv_cache, int32_
     return MLA_ERR_ALIGN;
   return hip_status(mla::launch_decode(q_lat, kv_cache, num_blocks, block_table, max_blocks,
                                        nullptr, B, q_len, n_h, dtype, softmax_scale, 1, work,
-                                       n_work, o_lat, lse, o_part, lse_part,
-                                       (hipStream_t)stream));
+                                       n_work, lists, lists ? n_lists : 0, o_lat, lse, o_part,
+                                       lse_part, (hipStream_t)stream));
 }
 
 int32_t mla_combine_planned(const float* o_part, const float* lse_part, const int32_t* split,

@@ -32,8 +32,8 @@ class DeviceProblem:
     """Device-resident inputs, cache and work buffers of one workload.
 
     num_splits > 0: uniform split-KV with that many splits per row.
-    num_splits == 0: a load-balanced work list from mla_plan_decode (``work``,
-    ``split``) sized for ``num_slots`` concurrent workgroups.
+    num_splits == 0: a load-balanced schedule from mla_plan_decode (``work``,
+    ``lists``, ``split``) sized for ``num_slots`` concurrent workgroups.
     """
     prob: Problem
     num_splits: int
@@ -57,6 +57,7 @@ class DeviceProblem:
     lse: object
     out: object
     work: Optional[object] = None
+    lists: Optional[object] = None
     split: Optional[object] = None
     n_parts: int = 0
 
@@ -123,12 +124,13 @@ def upload(prob: Problem, num_splits: Optional[int] = None, device="cuda",
                           ROPE_BASE)
     new_idx = prob.key_offsets[step_seq] + step_pos
     T = prob.T
-    work = split = None
+    work = lists = split = None
     n_parts = 0
     if S == 0:
         slots = device_slots(device) if num_slots is None else int(num_slots)
-        w, sp, n_parts = mla.mla_plan_decode(prob.seq_lens, wl.q_len, wl.n_h, slots)
+        w, ls, sp, n_parts = mla.mla_plan_decode(prob.seq_lens, wl.q_len, wl.n_h, slots)
         work = torch.from_numpy(w).to(device)
+        lists = torch.from_numpy(ls).to(device)
         split = torch.from_numpy(sp).to(device)
     n_part_rows = n_parts if S == 0 else (wl.B * S * wl.q_len if S > 1 else 0)
     dp = DeviceProblem(
@@ -149,7 +151,7 @@ def upload(prob: Problem, num_splits: Optional[int] = None, device="cuda",
         o_lat=torch.empty((T, wl.n_h, D_C), dtype=torch.float32, device=device),
         lse=torch.empty((T, wl.n_h), dtype=torch.float32, device=device),
         out=torch.empty((T, wl.n_h, D_H), dtype=torch.float32, device=device),
-        work=work, split=split, n_parts=n_parts,
+        work=work, lists=lists, split=split, n_parts=n_parts,
     )
     return dp
 
@@ -169,7 +171,8 @@ def decode(dp: DeviceProblem, stream=None):
     if S == 0:
         mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
                                      softmax_scale(), dp.work, dp.o_lat, dp.lse,
-                                     o_part=dp.o_part, lse_part=dp.lse_part, stream=stream)
+                                     o_part=dp.o_part, lse_part=dp.lse_part, lists=dp.lists,
+                                     stream=stream)
         if dp.split.shape[0] > 0:
             mla.mla_combine_planned(dp.o_part, dp.lse_part, dp.split, dp.n_h, dp.o_lat, dp.lse,
                                     stream=stream)
