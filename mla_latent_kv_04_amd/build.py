@@ -24,13 +24,15 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are not used in this library
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA accumulators in the VGPR form; the register allocator then
-    # places the long-lived query fragments in AGPRs
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# Keep compiler-generated MFMA accumulators in the VGPR form; the register
+# allocator then places long-lived operands in AGPRs.  decode_h64.hip is the
+# exception: its value waves keep their accumulators in AGPRs (AGPR form).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 SOURCES = ["kv_append.hip", "absorb_q.hip", "decode.hip", "decode_h64.hip", "combine.hip", "out_proj.hip",
            "mla_api.cpp"]
+EXTRA = {src: VGPR_FORM for src in SOURCES if src.endswith(".hip") and src != "decode_h64.hip"}
 
 
 def _hipcc() -> str:
@@ -42,7 +44,7 @@ def _hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
