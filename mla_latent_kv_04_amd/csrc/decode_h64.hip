@@ -10,7 +10,7 @@
 // of a unit are launched 8 workgroup ids apart, which places them on the same
 // XCD so the second read of every KV tile is served by that XCD's L2.
 //
-// Eight waves in two roles, two waves per SIMD (one of each role):
+// Eight waves in two roles:
 //
 //   score waves 0..3, (hq, th) = (w & 1, w >> 1): scores of heads
 //     32hq..32hq+31 against tokens 16th..16th+15 of a tile, with the query
@@ -24,20 +24,27 @@
 //     uses exactly the P of the numerator.  These waves also issue the
 //     direct-to-LDS loads of the tiles.
 //
-// While a score wave runs its softmax arithmetic, the value wave on its SIMD
-// keeps the matrix unit busy, and the other way round; the hardware does the
-// interleaving.  Tiles are 32 tokens (half a paged block) in four LDS stages,
-// loaded three tiles ahead.  Iteration a of the tile loop sits between two
-// workgroup barriers:
+// Each SIMD holds one wave of each role, and each iteration a of the tile
+// loop has two phases, so that one role's VALU and LDS work overlaps the
+// other's MFMAs (the hardware interleaves the two waves):
 //
-//   barrier a : tile a+1 has landed; P(a), its maxima and flags are in LDS;
-//               tile a-1 is no longer read by anyone
-//   score     : QK^T and softmax of tile a+1 (P(a+1) into the other P buffer)
-//   value     : PV of tile a; loads of tile a+3 into the stage of tile a-1
-//   [redo a]  : only if a score wave saw a score of tile a beat the running
-//               max by more than 2^8 (log2 domain): the score waves agree on
-//               the new max and rewrite P(a), then (second barrier) the value
-//               waves rescale their accumulators before reading P(a).
+//   barrier A(a): tile a+1 has landed; P(a), its maxima and flags are in LDS;
+//                 tile a-1 is no longer read by anyone
+//   phase A  score: QK^T of tile a+1 (36 MFMAs per wave)
+//            value: P(a) and V(a) into registers, PV of the first half of
+//                   the dims (16 MFMAs), loads of tile a+3 into the stage of
+//                   tile a-1
+//   barrier B(a)
+//   phase B  score: softmax of tile a+1 (scale, mask, tile maxima, P(a+1)
+//                   against the running max, into the other P buffer)
+//            value: PV of the second half of the dims, and the P row sums
+//   [redo a] only if a score wave saw a score of tile a beat the running max
+//            by more than 2^8 (log2 domain): in phase A the score waves agree
+//            on the new max and rewrite P(a), then (one more barrier) the
+//            value waves rescale their accumulators before reading P(a).
+//
+// Tiles are 32 tokens (half a paged block) in four LDS stages, loaded three
+// tiles ahead.
 //
 // LDS: four tile stages of 37,888 bytes (32 token rows at a 1168-byte pitch:
 // 72 16-byte chunks plus a pad chunk, which puts the 16 tokens of a K fragment
@@ -66,6 +73,14 @@ constexpr int NDMA = (NINST + 3) / 4;        // 10: instructions of value wave 0
 constexpr int KSTEPS = ROW / 32;             // 18
 constexpr int KSTEPS_A = 16;                 // query k-steps held in AGPRs (the rest in VGPRs)
 constexpr int IDCAP = 512;                   // block ids staged per chunk of an item
+#ifndef PV_PHASE_A
+#define PV_PHASE_A 4
+#endif
+#ifndef QK_REDO_STEP
+#define QK_REDO_STEP 6
+#endif
+constexpr int PV_A = PV_PHASE_A;             // PV dim blocks (of 8) run in phase A
+constexpr int QK_MID = QK_REDO_STEP;         // QK k-steps issued before the redo check
 
 // LDS map (bytes)
 constexpr int OFF_STAGE = 0;
@@ -339,11 +354,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
 #pragma unroll
           for (int ks = 0; ks < KPF; ++ks) kbuf[ks] = lds_b128(kp + ks * 64);
         };
-        auto score = [&](int a, int hi, i16x8_t (&kbuf)[KPF + 1]) {
+        // mid() runs after k-step QK_MID - 1 (the redo check: the scores of the
+        // next tile do not depend on it, so the MFMAs start first)
+        auto qk = [&](int a, int hi, i16x8_t (&kbuf)[KPF + 1], f32x4_t (&sc)[2], auto&& mid) {
           const char* kp = smem + ch.stage(a) + k_off;
           f32x4_t q4[2][2];
 #pragma unroll
           for (int ks = 0; ks < KSTEPS; ++ks) {
+            if (ks == QK_MID) mid();
             if (ks + KPF < KSTEPS) kbuf[(ks + KPF) % (KPF + 1)] = lds_b128(kp + (ks + KPF) * 64);
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
@@ -356,7 +374,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
             }
           }
           qk_drain(q4[0][0], q4[0][1], q4[1][0], q4[1][1]);
-          f32x4_t sc[2];
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) sc[hb] = (q4[hb][0] + q4[hb][1]) * scale_log2;
           const int lo = ch.lo(a);
@@ -369,6 +386,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
                 if (row < lo || row >= hi) sc[hb][i] = -INFINITY;
               }
           }
+        };
+        auto softmax = [&](int a, const f32x4_t (&sc)[2]) {
           const int par = ch.par(a);
           bool need = false;
 #pragma unroll
@@ -387,32 +406,41 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
         lds_sync();  // tile c0 has landed
         {
           i16x8_t kbuf[KPF + 1];
+          f32x4_t sc[2];
           k_first(c0, kbuf);
-          score(c0, ch.hi(c0), kbuf);
+          qk(c0, ch.hi(c0), kbuf, sc, [] {});
+          lds_sync();
+          softmax(c0, sc);
         }
         for (int a = c0; a < c1; ++a) {
-          lds_sync();  // barrier a
+          lds_sync();  // barrier A(a)
           const int par = ch.par(a);
           const int4 fl = *reinterpret_cast<const int4*>(flags + par * 4);
           const int hi_n = ch.hi(a + 1);
           i16x8_t kbuf[KPF + 1];
           k_first(a + 1, kbuf);
-          if (uniform(fl.x | fl.y | fl.z | fl.w) != 0) {
-            // rare: agree on the new running max from both token halves, record
-            // the rescale factors, rewrite P(a)
+          auto redo = [&] {
+            if (uniform(fl.x | fl.y | fl.z | fl.w) != 0) {
+              // rare: agree on the new running max from both token halves,
+              // record the rescale factors, rewrite P(a)
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-              const float mx =
-                  fmaxf(ml_keep[hb], maxbuf[(par * 2 + (th ^ 1)) * HG + hq * 32 + hb * 16 + r16]);
-              const float mnew = mx > mref[hb] + RESCALE_LOG2 ? mx : mref[hb];
-              const float f = fast_exp2(mref[hb] - mnew);
-              mref[hb] = mnew;
-              if (th == 0 && g == 0) fbuf[hq * 32 + hb * 16 + r16] = f;
+              for (int hb = 0; hb < 2; ++hb) {
+                const float mx =
+                    fmaxf(ml_keep[hb], maxbuf[(par * 2 + (th ^ 1)) * HG + hq * 32 + hb * 16 + r16]);
+                const float mnew = mx > mref[hb] + RESCALE_LOG2 ? mx : mref[hb];
+                const float f = fast_exp2(mref[hb] - mnew);
+                mref[hb] = mnew;
+                if (th == 0 && g == 0) fbuf[hq * 32 + hb * 16 + r16] = f;
+              }
+              write_p(a, sc_keep);
+              lds_sync();  // redone P and the factors are visible to the value waves
             }
-            write_p(a, sc_keep);
-            lds_sync();  // redone P and the factors are visible to the value waves
-          }
-          score(a + 1, hi_n, kbuf);  // past the chunk: fully masked, written but never read
+          };
+          // tile a+1 (past the chunk: fully masked; written but never read)
+          f32x4_t sc[2];
+          qk(a + 1, hi_n, kbuf, sc, redo);
+          lds_sync();  // barrier B(a)
+          softmax(a + 1, sc);
         }
         c0 = c1;
       }
@@ -499,11 +527,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
         if (extra) vm_wait<2 * NDMA>(); else vm_wait<2 * (NDMA - 1)>();
         lds_sync();  // tile c0 has landed
         if (ch.partial(c0)) zero_rows(c0);
+        lds_sync();  // the score waves' softmax of tile c0 follows
         for (int a = c0; a < c1; ++a) {
           // tile a+1 landed: its loads were issued two iterations ago; those of
           // the last iteration (tile a+2) may stay in flight
           if (extra) vm_wait<NDMA>(); else vm_wait<NDMA - 1>();
-          lds_sync();  // barrier a
+          lds_sync();  // barrier A(a)
           const int par = ch.par(a);
           const int4 fl = *reinterpret_cast<const int4*>(flags + par * 4);
           const int id_n = ch.id(a + 1);
@@ -522,8 +551,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
             rsum *= fbuf[wp * 16 + r16];
             asm volatile("s_nop 7");  // VALU-written accumulators, then MFMA reads
           }
-          // P(a) and all of V(a) first, then the loads of tile a+3 (LDS reads
-          // this wave issues after a direct-to-LDS load queue behind it)
+          // Phase A: P(a), all of V(a), PV of dims 16db.. for db < PV_A, then
+          // the loads of tile a+3 (LDS reads this wave issues after a
+          // direct-to-LDS load queue behind it).  Phase B: the rest of PV.
           const char* pb = smem + OFF_P + par * PBUF;
           i16x8_t pf[4];
 #pragma unroll
@@ -539,13 +569,17 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0 + 16 * RSLOTS * 16));
             vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           }
-          issue(a + 3, src, nid);
 #pragma unroll
-          for (int db = 0; db < 8; ++db) {
+          for (int db = 0; db < PV_A; ++db)
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb) mma_pv(acc[hb][db], vf[db], pf[hb]);
-            if (db == 3) mma_sum(rsum, ones, pw);
-          }
+          issue(a + 3, src, nid);
+          lds_sync();  // barrier B(a): the score waves turn to their softmax
+#pragma unroll
+          for (int db = PV_A; db < 8; ++db)
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) mma_pv(acc[hb][db], vf[db], pf[hb]);
+          mma_sum(rsum, ones, pw);
         }
         vm_wait<0>();  // the loads past the chunk land before its stages are reused
         c0 = c1;
