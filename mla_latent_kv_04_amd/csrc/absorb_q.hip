@@ -10,6 +10,14 @@
 // tile is staged in LDS once and read as the MFMA A operand (rows c, reduced
 // d) with the transposing LDS read, since W^UK is stored with c contiguous.
 // The query fragments (reduced d contiguous) come straight from memory.
+//
+// The A rows of the four 16-column MFMA blocks are permuted so that the
+// output lands row-contiguous: block cb's row m is latent column
+// 16 (m >> 2) + 4 cb + (m & 3), so after the four blocks a lane holds 16
+// consecutive columns of one query row and writes them with full-width
+// stores (four lanes cover a row's 64 columns).  The RoPE half of q_lat is
+// shared out over the eight column-chunk workgroups of a head, 4 of the 32
+// rotation pairs each.
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -21,19 +29,26 @@ constexpr int CCH = 64;        // latent columns per workgroup
 constexpr int TCH = 128;       // rows per workgroup (4 waves x 2 blocks of 16)
 
 template <class E> struct AbsorbLds;
-template <> struct AbsorbLds<BF16> { static constexpr int stride = 160; };  // bytes per d row
+// bf16: a 136-byte row pitch puts the four rows of a transposing read on
+// disjoint banks for the permuted column pattern (staged with 8-byte writes)
+template <> struct AbsorbLds<BF16> { static constexpr int stride = 136; };  // bytes per d row
 template <> struct AbsorbLds<F32> { static constexpr int stride = 272; };
 
 template <class E>
 __device__ __forceinline__ typename E::frag load_wt_frag(const char* lds, int d0, int c_local);
 
-// bf16: two transposing reads give this lane W[d0 + 0..3][c] and W[d0 + 4..7][c],
-// c = c_local (lane % 16 inside the 16-column block starting at c_local - lane%16).
+// Column of the tile that A row m of column block cb stands for.
+__device__ __forceinline__ int perm_col(int m, int cb) { return 16 * (m >> 2) + 4 * cb + (m & 3); }
+
+// bf16: two transposing reads give this lane (A row m = lane % 16)
+// W[d0 + 0..3][perm_col(m, cb)] and W[d0 + 4..7][perm_col(m, cb)]: the lane
+// that supplies columns 16 (s & 3) + 4 cb .. +3 of row d0 + (s >> 2) feeds
+// rows m with m >> 2 == s & 3.
 template <>
-__device__ __forceinline__ BF16::frag load_wt_frag<BF16>(const char* lds, int d0, int cblk) {
+__device__ __forceinline__ BF16::frag load_wt_frag<BF16>(const char* lds, int d0, int cb) {
   constexpr int S = AbsorbLds<BF16>::stride;
   const int s = lane_id() & 15;
-  const char* p = lds + (d0 + (s >> 2)) * S + (cblk + 4 * (s & 3)) * 2;
+  const char* p = lds + (d0 + (s >> 2)) * S + (16 * (s & 3) + 4 * cb) * 2;
   i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
   i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * S));
   BF16::frag f;
@@ -42,13 +57,31 @@ __device__ __forceinline__ BF16::frag load_wt_frag<BF16>(const char* lds, int d0
 }
 
 template <>
-__device__ __forceinline__ F32::frag load_wt_frag<F32>(const char* lds, int d0, int cblk) {
+__device__ __forceinline__ F32::frag load_wt_frag<F32>(const char* lds, int d0, int cb) {
   constexpr int S = AbsorbLds<F32>::stride;
-  const int c = cblk + (lane_id() & 15);
+  const int c = perm_col(lane_id() & 15, cb);
   F32::frag f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) f.v[j] = *reinterpret_cast<const float*>(lds + (d0 + j) * S + c * 4);
   return f;
+}
+
+// 16 consecutive outputs of one row, 16-byte aligned.
+template <class E>
+__device__ __forceinline__ void store16(typename E::storage* dst, const float (&v)[16]);
+template <>
+__device__ __forceinline__ void store16<BF16>(uint16_t* dst, const float (&v)[16]) {
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  d[0] = uint4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+               pack_bf16x2(v[6], v[7])};
+  d[1] = uint4{pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
+               pack_bf16x2(v[14], v[15])};
+}
+template <>
+__device__ __forceinline__ void store16<F32>(float* dst, const float (&v)[16]) {
+  float4* d = reinterpret_cast<float4*>(dst);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
 }
 
 template <class E>
@@ -64,18 +97,8 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
   const int t0 = blockIdx.z * TCH;
   const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
 
-  // Stage W^UK_h[0:128, c0:c0+64] (16-byte pieces).
-  constexpr int PER16 = 16 / E::bytes;
-  constexpr int PIECES_PER_ROW = CCH / PER16;
-  const T_* wsrc = w_uk + (long)h * D_H * D_C + c0;
-  for (int p = threadIdx.x; p < D_H * PIECES_PER_ROW; p += 256) {
-    const int d = p / PIECES_PER_ROW, q = p % PIECES_PER_ROW;
-    *reinterpret_cast<uint4*>(lds + d * S + q * 16) =
-        *reinterpret_cast<const uint4*>(wsrc + (long)d * D_C + q * PER16);
-  }
-  __syncthreads();
-
-  // Query fragments (B operand): lane holds row t = tb*16 + r16, d = ks*32 + 8g + j.
+  // Query fragments (B operand): lane holds row t = tb*16 + r16, d = ks*32 + 8g + j
+  // (issued first, so that they land while the weight tile is staged).
   typename E::frag qf[2][4];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
@@ -90,31 +113,26 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
       }
     }
   }
+  // Stage W^UK_h[0:128, c0:c0+64] (16-byte pieces, written as two halves:
+  // the bf16 row pitch is a multiple of 8 bytes only).
+  constexpr int PER16 = 16 / E::bytes;
+  constexpr int PIECES_PER_ROW = CCH / PER16;
+  const T_* wsrc = w_uk + (long)h * D_H * D_C + c0;
+  constexpr int NP = D_H * PIECES_PER_ROW / 256;   // pieces per thread
+  static_assert(D_H * PIECES_PER_ROW % 256 == 0, "pieces split evenly");
+  uint4 wv[NP];
 #pragma unroll
-  for (int cb = 0; cb < CCH / 16; ++cb) {
-    f32x4_t acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      typename E::frag wf = load_wt_frag<E>(lds, ks * 32 + 8 * g, cb * 16);
-      E::mma(acc[0], wf, qf[0][ks]);
-      E::mma(acc[1], wf, qf[1][ks]);
-    }
-    // D[c][t]: lane holds t = r16 (+16 tb), c = cb*16 + 4g + i.
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int t = t0 + wave * 32 + tb * 16 + r16;
-      if (t < T) {
-        T_* dst = q_lat + ((long)t * n_h + h) * ROW + c0 + cb * 16 + 4 * g;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = E::from_f32(acc[tb][i]);
-      }
-    }
+  for (int i = 0; i < NP; ++i) {
+    const int p = i * 256 + threadIdx.x, d = p / PIECES_PER_ROW, q = p % PIECES_PER_ROW;
+    wv[i] = *reinterpret_cast<const uint4*>(wsrc + (long)d * D_C + q * PER16);
   }
 
-  // Decoupled RoPE query, written once per (row, head) by the first column chunk.
-  if (blockIdx.y == 0) {
-    for (int e = threadIdx.x; e < TCH * (D_R / 2); e += 256) {
-      const int t = t0 + e / (D_R / 2), k = e % (D_R / 2);
+  // Decoupled RoPE query, this column chunk's 4 of the 32 rotation pairs (its
+  // float64 angle arithmetic runs while the loads above are in flight).
+  {
+    constexpr int KPW = (D_R / 2) / (D_C / CCH);  // pairs per workgroup
+    for (int e = threadIdx.x; e < TCH * KPW; e += 256) {
+      const int t = t0 + e / KPW, k = blockIdx.y * KPW + e % KPW;
       if (t >= T) break;
       double c, s;
       rope_cs(q_pos[t], k, base, c, s);
@@ -125,6 +143,43 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
       dst[2 * k + 1] = E::from_f32((float)(x * s + y * c));
     }
   }
+
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int p = i * 256 + threadIdx.x, d = p / PIECES_PER_ROW, q = p % PIECES_PER_ROW;
+    uint2* dst = reinterpret_cast<uint2*>(lds + d * S + q * 16);
+    dst[0] = uint2{wv[i].x, wv[i].y};
+    dst[1] = uint2{wv[i].z, wv[i].w};
+  }
+  __syncthreads();
+
+  f32x4_t acc[2][CCH / 16];
+#pragma unroll
+  for (int cb = 0; cb < CCH / 16; ++cb) {
+    acc[0][cb] = f32x4_t{0, 0, 0, 0};
+    acc[1][cb] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      typename E::frag wf = load_wt_frag<E>(lds, ks * 32 + 8 * g, cb);
+      E::mma(acc[0][cb], wf, qf[0][ks]);
+      E::mma(acc[1][cb], wf, qf[1][ks]);
+    }
+  }
+  // D[m][t] of block cb: lane holds t = r16 (+16 tb) and m = 4g + i, i.e.
+  // column perm_col(4g + i, cb) = 16g + 4cb + i: columns 16g .. 16g + 15.
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int t = t0 + wave * 32 + tb * 16 + r16;
+    if (t < T) {
+      float v[16];
+#pragma unroll
+      for (int cb = 0; cb < CCH / 16; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * cb + i] = acc[tb][cb][i];
+      store16<E>(q_lat + ((long)t * n_h + h) * ROW + c0 + 16 * g, v);
+    }
+  }
+
 }
 
 }  // namespace

@@ -8,7 +8,13 @@
 // fragments load straight from memory.  For bf16 weights the fp32 latent
 // output is split as hi + lo with hi = bf16(x), lo = bf16(x - hi) and both
 // halves are multiplied (16 significant bits of o_lat instead of 8).
-// One workgroup per (head, 64 rows); wave w owns output rows d in [32w, 32w+32).
+// One workgroup per (head, 64 rows).  bf16 weights: the head's W^UV (128 x
+// 512, 128 KB at a 1040-byte row pitch, which puts the 16 rows of an MFMA
+// fragment read on disjoint banks) is staged in LDS once; wave w owns query
+// rows 16w .. 16w + 15 of the chunk and all 128 outputs, so every o_lat
+// element is read from memory once.  fp32 weights (too large to stage):
+// wave w owns output rows d in [32w, 32w+32) and reads both operands from
+// memory.
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -23,14 +29,13 @@ template <class E> struct LatFrag;
 template <> struct LatFrag<BF16> {
   static constexpr int parts = 2;
   __device__ static void load(const float* p, bool ok, BF16::frag* f) {
-    float x[8];
-    if (ok) {
-      const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = 0.0f;
-    }
+    if (ok)
+      split(reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1], f);
+    else
+      split(float4{0, 0, 0, 0}, float4{0, 0, 0, 0}, f);
+  }
+  __device__ static void split(const float4& a, const float4& b, BF16::frag* f) {
+    float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     float lo[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -54,6 +59,97 @@ template <> struct LatFrag<F32> {
     }
   }
 };
+
+constexpr int WPITCH = D_C * 2 + 16;   // bytes per staged bf16 W^UV row
+
+// One direct-to-LDS load: lane l's 16 bytes from base + lane_off land at LDS
+// byte lds_dst + 16 l (M0 holds the LDS address; one wait state before use).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is named as clobbered on purpose
+__device__ __forceinline__ void dma_row(unsigned lds_dst, const char* base, unsigned lane_off) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %2"
+      :
+      : "v"(lane_off), "s"(lds_dst), "s"(base)
+      : "m0");
+}
+#pragma clang diagnostic pop
+
+// Workgroup (h, y) runs row chunks y, y + gridDim.y, ... of head h against
+// one staged copy of W^UV_h.
+__global__ void __launch_bounds__(256) out_proj_bf16_kernel(const float* __restrict__ o_lat,
+                                                            const uint16_t* __restrict__ w_uv,
+                                                            int T, int n_h, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) char wl[D_H * WPITCH];   // [128][WPITCH]
+  const int h = blockIdx.x;
+  const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+
+  // This lane's o_lat operand (query row t, columns 32ks + 8g .. +7 for all
+  // 16 k-steps), loaded whole: one workgroup fits a CU, so registers are
+  // plentiful, and the first chunk's loads land while W^UV is staged.
+  float4 raw[D_C / 32][2];
+  auto load_rows = [&](int t) {
+    const bool ok = t < T;
+    const float4* lrow = reinterpret_cast<const float4*>(o_lat + ((long)t * n_h + h) * D_C + 8 * g);
+#pragma unroll
+    for (int ks = 0; ks < D_C / 32; ++ks) {
+      raw[ks][0] = ok ? lrow[ks * 8] : float4{0, 0, 0, 0};
+      raw[ks][1] = ok ? lrow[ks * 8 + 1] : float4{0, 0, 0, 0};
+    }
+  };
+  load_rows(blockIdx.y * TCH + wave * 16 + r16);
+
+  // stage W^UV_h with direct-to-LDS loads, all in flight at once: one
+  // 64-lane instruction moves one 1024-byte row into its padded LDS row;
+  // wave w moves rows w, w + 4, ...
+  {
+    const char* wh = reinterpret_cast<const char*>(w_uv + (long)h * D_H * D_C);
+    const unsigned wl_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)wl;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll 8
+    for (int r = wave_u; r < D_H; r += 4)
+      dma_row(wl_base + r * WPITCH, wh + (long)r * D_C * 2, lane * 16);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's rows (and o_lat loads) landed
+  }
+  __syncthreads();
+
+  for (int t0 = blockIdx.y * TCH; t0 < T; t0 += gridDim.y * TCH) {
+  // the weight fragments do not depend on the chunk: keep the compiler from
+  // hoisting all 128 of them (512 registers) out of this loop
+  asm volatile("" ::: "memory");
+  const int t = t0 + wave * 16 + r16;
+  // D[d][t] = sum_c W[d][c] o_lat[t][c]: A = W rows d (LDS), B = o_lat rows t
+  // split into bf16 hi + lo.
+  f32x4_t acc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc[db] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < D_C / 32; ++ks) {
+    BF16::frag lf[2];
+    LatFrag<BF16>::split(raw[ks][0], raw[ks][1], lf);
+    const char* wp = wl + r16 * WPITCH + (ks * 32 + 8 * g) * 2;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      BF16::frag wf;
+      wf.v = *reinterpret_cast<const i16x8_t*>(wp + db * 16 * WPITCH);
+      BF16::mma(acc[db], wf, lf[0]);
+      BF16::mma(acc[db], wf, lf[1]);
+    }
+  }
+  // the next chunk's rows, while this one's outputs are written
+  if (t0 + gridDim.y * TCH < T) load_rows(t + gridDim.y * TCH);
+  // lane holds t = r16 and d = 16db + 4g + i
+  if (t < T) {
+    float* orow = out + ((long)t * n_h + h) * D_H + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      *reinterpret_cast<float4*>(orow + db * 16) =
+          float4{acc[db][0], acc[db][1], acc[db][2], acc[db][3]};
+  }
+  }
+}
 
 template <class E>
 __global__ void __launch_bounds__(256) out_proj_kernel(const float* __restrict__ o_lat,
@@ -101,10 +197,14 @@ __global__ void __launch_bounds__(256) out_proj_kernel(const float* __restrict__
 hipError_t launch_out_proj(const float* o_lat, const void* w_uv, int T, int n_h, int dtype,
                            float* out, hipStream_t stream) {
   dim3 grid(n_h, (T + TCH - 1) / TCH), block(256);
-  if (dtype == 1)
-    hipLaunchKernelGGL(out_proj_kernel<BF16>, grid, block, 0, stream, o_lat,
-                       (const uint16_t*)w_uv, T, n_h, out);
-  else
+  if (dtype == 1) {
+    // about two workgroups per CU of (head, chunk) pairs; each stages W^UV_h
+    // once for all of its chunks
+    const int chunks = (T + TCH - 1) / TCH;
+    const int per_wg = max(1, (chunks * n_h + 511) / 512);
+    hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(n_h, (chunks + per_wg - 1) / per_wg), block, 0,
+                       stream, o_lat, (const uint16_t*)w_uv, T, n_h, out);
+  } else
     hipLaunchKernelGGL(out_proj_kernel<F32>, grid, block, 0, stream, o_lat, (const float*)w_uv, T,
                        n_h, out);
   return hipGetLastError();
