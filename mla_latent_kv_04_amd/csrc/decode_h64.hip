@@ -46,12 +46,11 @@
 // Tiles are 32 tokens (half a paged block) in four LDS stages, loaded three
 // tiles ahead.
 //
-// LDS: four tile stages of 37,888 bytes (32 token rows at a 1168-byte pitch:
-// 72 16-byte chunks plus a pad chunk, which puts the 16 tokens of a K fragment
-// and the 4 tokens of a transposing V read on disjoint banks, and makes every
-// direct-to-LDS instruction read consecutive chunks of a row), two P buffers,
-// two sets of tile maxima and flags, rescale factors, and the block ids of the
-// current item.
+// LDS: four tile stages of 36,864 bytes (32 token rows of 72 16-byte chunks,
+// swizzled inside 256-byte groups so that the K and V fragment reads are free
+// of bank conflicts; one tile is exactly 36 direct-to-LDS instructions), two
+// P buffers, two sets of tile maxima and flags, rescale factors, and the block
+// ids of the current item.
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -66,10 +65,10 @@ constexpr int NTHREADS = 512;                // 4 score waves + 4 value waves
 constexpr int HG = 64;                       // heads per workgroup
 constexpr int TT = 32;                       // tokens per tile (half a paged block)
 constexpr int NSTAGE = 4;                    // tile stages in LDS
-constexpr int RSLOTS = ROW * 2 / 16 + 1;     // 73 16-byte slots per token row: 72 + 1 pad
-constexpr int NINST = (TT * RSLOTS + 63) / 64;   // 37 direct-to-LDS instructions per tile
-constexpr int STAGE = NINST * 1024;          // 37,888 bytes (tile + spill-over room)
-constexpr int NDMA = (NINST + 3) / 4;        // 10: instructions of value wave 0 (the others issue 9)
+constexpr int RSLOTS = ROW * 2 / 16;         // 72 16-byte chunks per token row
+constexpr int NINST = TT * RSLOTS / 64;      // 36 direct-to-LDS instructions per tile
+constexpr int STAGE = NINST * 1024;          // 36,864 bytes
+constexpr int NDMA = NINST / 4;              // 9 per value wave
 constexpr int KSTEPS = ROW / 32;             // 18
 constexpr int KSTEPS_A = 16;                 // query k-steps held in AGPRs (the rest in VGPRs)
 constexpr int IDCAP = 512;                   // block ids staged per chunk of an item
@@ -93,7 +92,7 @@ constexpr int OFF_IDS = OFF_FLAG + 2 * 4 * 4;         // int [IDCAP]
 constexpr int OFF_ONES = OFF_IDS + IDCAP * 4;         // 8 bf16 ones
 constexpr int SMEM = OFF_ONES + 16;
 static_assert(SMEM <= 163840, "LDS budget");
-static_assert(TT * RSLOTS * 16 <= STAGE, "tile fits its stage");
+static_assert(TT * RSLOTS * 16 == STAGE && NINST % 4 == 0, "a tile is whole load instructions");
 
 // ---------------------------------------------------------------------------
 // Direct-to-LDS loads.  Instruction j (0..36) of a tile fills stage slots
@@ -125,15 +124,28 @@ __device__ __forceinline__ void dma_one(unsigned lds_dst, const char* base, unsi
 }
 #pragma clang diagnostic pop
 
-// Byte offset, in the tile's half block, of lane l's slot of instruction j.
+// LDS layout of a tile: token row t occupies 72 consecutive 16-byte slots;
+// chunk f of the row (bytes 16f .. 16f + 15 of its 1152) sits at slot
+// f ^ swz(t) inside its aligned group of 16 chunks (the last, 8-chunk group
+// uses swz(t) & 7).  With swz(t) = (t & 7) ^ 5 (t >> 3) neither the 16-byte K
+// fragment reads (16 rows x 4 chunks per instruction) nor the transposing V
+// reads (8 rows x 32 bytes per 32 lanes) hit an LDS bank twice in a cycle, as
+// the LDS bank-conflict counters confirm; an unswizzled row pitch of 72 or 73
+// chunks costs those reads about twice their conflict-free time.
+__device__ __forceinline__ int swz(int t) { return (t & 7) ^ (5 * (t >> 3)); }
+__device__ __forceinline__ int chunk_slot(int t, int f) {
+  return f < 64 ? (f ^ swz(t)) : 64 + ((f - 64) ^ (swz(t) & 7));
+}
+
+// Byte offset, in the tile's half block, of the chunk that lane l of
+// instruction j moves: the instruction fills stage slots 64j .. 64j + 63 in
+// order, slot s = 64j + l being position s % 72 of row s / 72.  The
+// swizzle permutes chunks inside aligned 256-byte groups, so the 16 lanes of
+// a group still read one contiguous 256-byte piece of the row.
 __device__ __forceinline__ unsigned dma_src(int j, int lane) {
   const int slot = 64 * j + lane;
-  int tok = slot / RSLOTS, f = slot - tok * RSLOTS;
-  if (tok >= TT) {
-    tok = TT - 1;
-    f = RSLOTS - 2;
-  }
-  return (unsigned)(tok * (ROW * 2) + min(f, RSLOTS - 2) * 16);
+  const int t = slot / RSLOTS, p = slot - t * RSLOTS;
+  return (unsigned)(t * (ROW * 2) + chunk_slot(t, p) * 16);   // the slot map is an involution
 }
 
 // s_waitcnt vmcnt(N) with the other counters untouched (gfx9 encoding).
@@ -226,15 +238,19 @@ struct Chunk {
 
 // Stage the block ids of blocks [blk0, blk0 + nblk) of a sequence (out-of-range
 // ids become -1: a missing block).  Both barriers are workgroup-wide: the first
-// waits until every wave is done with the previous chunk's buffers.
-__device__ __forceinline__ void stage_ids(int* ids, const int* trow, int blk0, int nblk,
+// waits until every wave is done with the previous chunk's buffers.  Returns
+// whether any block of the chunk is missing (the same value in every thread).
+__device__ __forceinline__ bool stage_ids(int* ids, const int* trow, int blk0, int nblk,
                                           int num_blocks) {
   __syncthreads();
+  bool missing = false;
   for (int e = threadIdx.x; e < nblk; e += NTHREADS) {
     const int id = trow[blk0 + e];
-    ids[e] = (id >= 0 && id < num_blocks) ? id : -1;
+    const bool ok = id >= 0 && id < num_blocks;
+    ids[e] = ok ? id : -1;
+    missing |= !ok;
   }
-  __syncthreads();
+  return __syncthreads_or(missing) != 0;
 }
 
 __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
@@ -290,8 +306,15 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
   if (wave < 4) {
     // =========================== score waves ===========================
     const int hq = wave & 1, th = wave >> 1;
-    // K fragment: token 16th + r16, chunk 4ks + g (bytes from the stage start)
-    const int k_off = ((16 * th + r16) * RSLOTS + g) * 16;
+    // K fragment of k-step ks: token 16th + r16, chunk 4ks + g, at byte
+    // k_addr(ks) of the stage (the swizzle leaves bits 4.. of the chunk alone)
+    const int t_k = 16 * th + r16;
+    int kq[4], kq2[2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kq[q] = (t_k * RSLOTS + ((4 * q + g) ^ swz(t_k))) * 16;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) kq2[q] = (t_k * RSLOTS + 64 + ((4 * q + g) ^ (swz(t_k) & 7))) * 16;
+    auto k_addr = [&](int ks) { return ks < 16 ? kq[ks & 3] + 256 * (ks >> 2) : kq2[ks - 16]; };
     constexpr int KPF = 3;  // K fragments are read KPF steps ahead
 
     for (int item = i_begin; item < i_end; ++item) {
@@ -350,19 +373,19 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
         // anyway, is then replaced in a redo).  Every lane of a group writes the
         // same maximum and every lane the same flag: no branches.
         auto k_first = [&](int a, i16x8_t (&kbuf)[KPF + 1]) {
-          const char* kp = smem + ch.stage(a) + k_off;
+          const char* kp = smem + ch.stage(a);
 #pragma unroll
-          for (int ks = 0; ks < KPF; ++ks) kbuf[ks] = lds_b128(kp + ks * 64);
+          for (int ks = 0; ks < KPF; ++ks) kbuf[ks] = lds_b128(kp + k_addr(ks));
         };
         // mid() runs after k-step QK_MID - 1 (the redo check: the scores of the
         // next tile do not depend on it, so the MFMAs start first)
         auto qk = [&](int a, int hi, i16x8_t (&kbuf)[KPF + 1], f32x4_t (&sc)[2], auto&& mid) {
-          const char* kp = smem + ch.stage(a) + k_off;
+          const char* kp = smem + ch.stage(a);
           f32x4_t q4[2][2];
 #pragma unroll
           for (int ks = 0; ks < KSTEPS; ++ks) {
             if (ks == QK_MID) mid();
-            if (ks + KPF < KSTEPS) kbuf[(ks + KPF) % (KPF + 1)] = lds_b128(kp + (ks + KPF) * 64);
+            if (ks + KPF < KSTEPS) kbuf[(ks + KPF) % (KPF + 1)] = lds_b128(kp + k_addr(ks + KPF));
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
               if (ks < 2)
@@ -465,10 +488,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
     const int d0 = wp * 128;                   // first output dim of this wave
     unsigned lane_src[NDMA];
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) lane_src[i] = dma_src(min(wp + 4 * i, NINST - 1), lane);
-    const bool extra = wp + 4 * (NDMA - 1) < NINST;   // value wave 0 issues 10, the others 9
-    // V^T fragment: tokens 4g + (r16 >> 2) (and +16), dims d0 + 16db + 4 (r16 & 3)
-    const int v_off = (4 * g + (r16 >> 2)) * RSLOTS * 16 + (d0 + 4 * (r16 & 3)) * 2;
+    for (int i = 0; i < NDMA; ++i) lane_src[i] = dma_src(wp + 4 * i, lane);
+    // V^T fragment of dims d0 + 16db ..: token t = 4g + (r16 >> 2) (and t + 16),
+    // dims d0 + 16db + 4 (r16 & 3) .. +3, i.e. chunk d0 / 8 + 2db + b of the
+    // row, bytes h8 .. h8 + 7 of it
+    const int t_v = 4 * g + (r16 >> 2), b_v = (r16 & 3) >> 1, h8 = (r16 & 1) * 8;
+    const int v_lo = t_v * RSLOTS * 16 + d0 * 2 + h8, v_hi = v_lo + 16 * RSLOTS * 16;
+    const int s_lo = swz(t_v), s_hi = swz(t_v + 16);
     const i16x8_t ones = lds_b128(smem + OFF_ONES);
 
     for (int item = i_begin; item < i_end; ++item) {
@@ -491,7 +517,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
       for (int c0 = t_first; c0 < t_last;) {
         const int c1 = min(t_last, (c0 & ~1) + 2 * IDCAP);
         const int blk0 = c0 >> 1;
-        stage_ids(ids, trow, blk0, ((c1 - 1) >> 1) - blk0 + 1, num_blocks);
+        const bool missing = stage_ids(ids, trow, blk0, ((c1 - 1) >> 1) - blk0 + 1, num_blocks);
         const Chunk ch{ids, c0, c1, blk0, kb, ke};
 
         // loads of tile `src` into the stage of tile `dst` (src == dst except
@@ -503,8 +529,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
           const char* base = cache_bytes + (long)id * (BLOCK * ROW * 2) + (src & 1) * (TT * ROW * 2);
           const unsigned to = lds_base + (unsigned)(ch.stage(dst) + wp * 1024);
 #pragma unroll
-          for (int i = 0; i < NDMA - 1; ++i) dma_one(to + i * 4096, base, lane_src[i]);
-          if (extra) dma_one(to + (NDMA - 1) * 4096, base, lane_src[NDMA - 1]);
+          for (int i = 0; i < NDMA; ++i) dma_one(to + i * 4096, base, lane_src[i]);
         };
         // rows outside [lo, hi) of tile a hold other keys or undefined data;
         // P = 0 there, so zero them (0 * NaN would not vanish).  The score
@@ -524,21 +549,44 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
         issue(c0, c0, load_id(c0));
         issue(c0 + 1, c0 + 1 < c1 ? c0 + 1 : c0, load_id(c0 + 1 < c1 ? c0 + 1 : c0));
         issue(c0 + 2, c0 + 2 < c1 ? c0 + 2 : c0, load_id(c0 + 2 < c1 ? c0 + 2 : c0));
-        if (extra) vm_wait<2 * NDMA>(); else vm_wait<2 * (NDMA - 1)>();
+        vm_wait<2 * NDMA>();
         lds_sync();  // tile c0 has landed
         if (ch.partial(c0)) zero_rows(c0);
         lds_sync();  // the score waves' softmax of tile c0 follows
         for (int a = c0; a < c1; ++a) {
           // tile a+1 landed: its loads were issued two iterations ago; those of
           // the last iteration (tile a+2) may stay in flight
-          if (extra) vm_wait<NDMA>(); else vm_wait<NDMA - 1>();
+          vm_wait<NDMA>();
           lds_sync();  // barrier A(a)
           const int par = ch.par(a);
+          // Every LDS read of phase A is issued at once: the flags, the block
+          // ids of tiles a+1 and a+3, P(a) and V(a).  P(a) changes only in a
+          // redo, which reads it again.  Then PV of dims 16db.. for db < PV_A,
+          // then the loads of tile a+3 (LDS reads this wave issues after a
+          // direct-to-LDS load queue behind it).  Phase B: the rest of PV.
           const int4 fl = *reinterpret_cast<const int4*>(flags + par * 4);
-          const int id_n = ch.id(a + 1);
           const int src = a + 3 < c1 ? a + 3 : a;
-          const int nid = load_id(src);
-          if (a + 1 < c1 && (ch.lo(a + 1) > 0 || ch.hi_of(a + 1, id_n) < TT)) zero_rows(a + 1);
+          const int id_src = ch.id(src);
+          const char* pb = smem + OFF_P + par * PBUF;
+          i16x8_t pf[4];
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) pf[hb] = lds_b128(pb + (hb * 64 + lane) * 16);
+          i16x8_t pw = lds_b128(pb + (wp * 64 + lane) * 16);
+          const char* vp = smem + ch.stage(a);
+          i16x8_t vf[8];
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)(vp + v_lo + ((2 * db + b_v) ^ s_lo) * 16));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)(vp + v_hi + ((2 * db + b_v) ^ s_hi) * 16));
+            vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+          // (the block id matters only in a chunk with a missing block; reading
+          // it otherwise would make this test wait for all of the reads above)
+          bool zero_next = a + 1 < c1 && (ch.lo(a + 1) > 0 || ke - (a + 1) * TT < TT);
+          if (missing && a + 1 < c1) zero_next = zero_next || uniform(ch.id(a + 1)) < 0;
+          if (zero_next) zero_rows(a + 1);
           if (uniform(fl.x | fl.y | fl.z | fl.w) != 0) {
             lds_sync();  // the score waves have rewritten P(a) and the factors
             asm volatile("s_nop 7");  // last PV MFMA results written back
@@ -550,25 +598,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
             }
             rsum *= fbuf[wp * 16 + r16];
             asm volatile("s_nop 7");  // VALU-written accumulators, then MFMA reads
-          }
-          // Phase A: P(a), all of V(a), PV of dims 16db.. for db < PV_A, then
-          // the loads of tile a+3 (LDS reads this wave issues after a
-          // direct-to-LDS load queue behind it).  Phase B: the rest of PV.
-          const char* pb = smem + OFF_P + par * PBUF;
-          i16x8_t pf[4];
 #pragma unroll
-          for (int hb = 0; hb < 4; ++hb) pf[hb] = lds_b128(pb + (hb * 64 + lane) * 16);
-          const i16x8_t pw = lds_b128(pb + (wp * 64 + lane) * 16);
-          const char* vp = smem + ch.stage(a) + v_off;
-          i16x8_t vf[8];
-#pragma unroll
-          for (int db = 0; db < 8; ++db) {
-            const char* p0 = vp + db * 32;
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
-            const i16x4_t hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0 + 16 * RSLOTS * 16));
-            vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            for (int hb = 0; hb < 4; ++hb) pf[hb] = lds_b128(pb + (hb * 64 + lane) * 16);
+            pw = lds_b128(pb + (wp * 64 + lane) * 16);
           }
+          const int nid = uniform(max(id_src, 0));
 #pragma unroll
           for (int db = 0; db < PV_A; ++db)
 #pragma unroll
