@@ -166,6 +166,36 @@ def test_decode_matches_latent_attention_on_its_inputs(case):
             1.0, float(np.abs(ll[fin]).max(initial=1)))
 
 
+def test_long_item_crosses_staged_block_id_chunks():
+    """A single work item of 625 blocks: the attention kernels stage at most
+    512 block ids at a time, so the item runs as two chunks with the softmax
+    state carried across."""
+    prob = small(F4, B=1, ctx=40000)
+    say("long item, two chunks")
+    dp = run_step(prob, num_splits=1)
+    out = to_np(dp.out)
+    ref, _, _ = oracle_sequence(prob, 0, heads=[0, 77, 127])
+    assert rel_err(out[0:1][:, [0, 77, 127]], ref) <= TOL[prob.wl.dtype]
+
+
+@pytest.mark.parametrize("splits", [1, 0])
+def test_rising_scores_force_running_max_updates(splits):
+    """Cached rows scaled up tile by tile, so the scores keep beating the
+    running maximum mid-sequence: the online softmax's rescaling (and, in the
+    64-head kernel, its rewrite of P) runs on most tiles."""
+    prob = small(F3, B=2, ctx=[1500, 3000])
+    pos = np.concatenate([np.arange(int(L)) for L in prob.seq_lens])
+    f = (1.0 + pos // 32)[:, None]
+    prob.c_kv = round_to_bf16(prob.c_kv * f)
+    prob.k_r = round_to_bf16(prob.k_r * f)
+    say(f"rising scores S={splits}")
+    dp = run_step(prob, num_splits=splits)
+    out = to_np(dp.out)
+    for b in range(2):
+        ref, _, _ = oracle_sequence(prob, b, heads=[0, 31, 64, 127])
+        assert rel_err(out[b:b + 1][:, [0, 31, 64, 127]], ref) <= TOL[prob.wl.dtype], b
+
+
 def test_combine_matches_oracle():
     import torch
     from mla_latent_kv_04_amd import _binding as mla
