@@ -175,10 +175,11 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if splits == 0:
-            if dp.split.shape[0] > 0:
-                mla.mla_combine_planned(dp.o_part, dp.lse_part, dp.split, dp.n_h, dp.o_lat,
-                                        dp.lse)
-        elif splits > 1:
+            # the split rows' merge runs inside the projection's loads
+            mla.mla_out_proj_planned(dp.o_lat, dp.o_part, dp.lse_part, dp.split, dp.w_uv,
+                                     dp.out, dp.lse)
+            return
+        if splits > 1:
             mla.mla_splitkv_combine(dp.o_part, dp.lse_part, dp.B, splits, dp.q_len, dp.n_h,
                                     dp.o_lat, dp.lse)
         mla.mla_out_proj(dp.o_lat, dp.w_uv, dp.out)

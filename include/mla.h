@@ -183,7 +183,7 @@ int32_t mla_splitkv_combine(const float* o_part, const float* lse_part, int32_t 
  * [T, n_h, 128].  For bf16 weights o_lat is split as hi + lo with
  * hi = bf16(x), lo = bf16(x - hi), so 16 significant bits of o_lat enter the
  * product instead of 8.
- * n_h must be a multiple of 16.  T == 0 is a no-op.
+ * T == 0 is a no-op.
  */
 int32_t mla_out_proj(const float* o_lat, const void* w_uv, int32_t T, int32_t n_h,
                      int32_t dtype, float* out, void* stream);
@@ -258,6 +258,22 @@ int32_t mla_decode_paged_planned(const void* q_lat, const void* kv_cache, int32_
  */
 int32_t mla_combine_planned(const float* o_part, const float* lse_part, const int32_t* split,
                             int32_t n_split, int32_t n_h, float* o_lat, float* lse, void* stream);
+
+/*
+ * mla_out_proj_planned - mla_combine_planned followed by mla_out_proj, in one
+ * pass for bf16 weights: the split rows of a plan (split device int32
+ * [n_split, 3] from mla_plan_decode, rows distinct and increasing) are merged
+ * from o_part / lse_part with the log-sum-exp rule of mla_splitkv_combine as
+ * they are loaded, and their LSE is written to lse (device fp32 [T, n_h], may
+ * be NULL); every other row is read from o_lat.  The merged rows of o_lat are
+ * scratch: after the call they hold either the merged value (fp32 weights,
+ * which run the two steps one after the other) or what they held before.
+ * Other arguments, layouts and the bf16 hi + lo split of the operand as in
+ * mla_out_proj.  0 <= n_split <= T; T == 0 is a no-op.
+ */
+int32_t mla_out_proj_planned(float* o_lat, const float* o_part, const float* lse_part,
+                             const int32_t* split, int32_t n_split, const void* w_uv, int32_t T,
+                             int32_t n_h, int32_t dtype, float* out, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,8 @@ D_C, D_R, D_H, ROW, BLOCK = 512, 64, 128, 576, 64
 
 _EXPORTS = ("mla_status_string", "mla_abi_version", "mla_kv_append", "mla_absorb_q",
             "mla_decode_paged", "mla_splitkv_combine", "mla_out_proj", "mla_split_plan",
-            "mla_plan_decode", "mla_decode_paged_planned", "mla_combine_planned")
+            "mla_plan_decode", "mla_decode_paged_planned", "mla_combine_planned",
+            "mla_out_proj_planned")
 
 
 class MLAError(RuntimeError):
@@ -63,6 +64,7 @@ def load() -> ctypes.CDLL:
         "mla_decode_paged_planned": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _F, _P, _I,
                                           _P, _I, _P, _P, _P, _P, _P]),
         "mla_combine_planned": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
+        "mla_out_proj_planned": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -317,3 +319,25 @@ def mla_combine_planned(o_part, lse_part, split, n_h, o_lat, lse=None, stream=No
                                     int(n_h), _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32),
                                     _stream(stream))
     _check("mla_combine_planned", st)
+
+
+def mla_out_proj_planned(o_lat, o_part, lse_part, split, w_uv, out, lse=None, stream=None):
+    """Merge a plan's split rows and project every row through W^UV (see mla.h).
+    The split rows of o_lat are scratch."""
+    torch = _torch()
+    f32 = torch.float32
+    dt = _dtype_code(w_uv)
+    T, n_h = int(o_lat.shape[0]), int(o_lat.shape[1])
+    if tuple(o_lat.shape) != (T, n_h, D_C) or tuple(w_uv.shape) != (n_h, D_H, D_C):
+        raise ValueError("o_lat must be [T, n_h, 512] and w_uv [n_h, 128, 512]")
+    if tuple(out.shape) != (T, n_h, D_H):
+        raise ValueError("out must be [T, n_h, 128]")
+    if split.dim() != 2 or split.shape[1] != 3:
+        raise ValueError("split must be [n_split, 3]")
+    n_split = int(split.shape[0])
+    st = load().mla_out_proj_planned(
+        _dev(o_lat, "o_lat", f32), _dev(o_part, "o_part", f32) if n_split else None,
+        _dev(lse_part, "lse_part", f32) if n_split else None,
+        _dev(split, "split", torch.int32) if n_split else None, n_split, _dev(w_uv, "w_uv"), T,
+        n_h, dt, _dev(out, "out", f32), _dev(lse, "lse", f32), _stream(stream))
+    _check("mla_out_proj_planned", st)

@@ -237,6 +237,21 @@ int32_t mla_out_proj(const float* o_lat, const void* w_uv, int32_t T, int32_t n_
   return hip_status(mla::launch_out_proj(o_lat, w_uv, T, n_h, dtype, out, (hipStream_t)stream));
 }
 
+int32_t mla_out_proj_planned(float* o_lat, const float* o_part, const float* lse_part,
+                             const int32_t* split, int32_t n_split, const void* w_uv, int32_t T,
+                             int32_t n_h, int32_t dtype, float* out, float* lse, void* stream) {
+  if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  if (T < 0 || n_h < 1 || n_split < 0 || n_split > T) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  if (n_split > 0 && (!o_part || !lse_part || !split)) return MLA_ERR_NULL;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  if (n_split > 0 && (!aligned16(o_part) || !aligned4(lse_part) || (lse && !aligned4(lse))))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_out_proj_planned(o_lat, o_part, lse_part, split, n_split, w_uv, T,
+                                                 n_h, dtype, out, lse, (hipStream_t)stream));
+}
+
 int32_t mla_split_plan(const int32_t* seq_lens, int32_t B, int32_t block_size, int32_t num_splits,
                        int32_t* begin_end) {
   if (B < 0 || num_splits < 1 || block_size != MLA_BLOCK) return MLA_ERR_SHAPE;

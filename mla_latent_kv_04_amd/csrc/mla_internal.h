@@ -45,4 +45,8 @@ hipError_t launch_combine_planned(const float* o_part, const float* lse_part, co
 hipError_t launch_out_proj(const float* o_lat, const void* w_uv, int T, int n_h, int dtype,
                            float* out, hipStream_t stream);
 
+hipError_t launch_out_proj_planned(float* o_lat, const float* o_part, const float* lse_part,
+                                   const int* split, int n_split, const void* w_uv, int T, int n_h,
+                                   int dtype, float* out, float* lse, hipStream_t stream);
+
 }  // namespace mla

@@ -15,6 +15,11 @@
 // element is read from memory once.  fp32 weights (too large to stage):
 // wave w owns output rows d in [32w, 32w+32) and reads both operands from
 // memory.
+//
+// The planned variant also finishes a balanced split-KV schedule: a row that
+// the schedule cut into several key ranges has its partial outputs merged
+// with the log-sum-exp rule (each part weighted by exp(lse_k - LSE)) as the
+// row's o_lat operand is loaded, so the merged row never goes to memory.
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -77,11 +82,62 @@ __device__ __forceinline__ void dma_row(unsigned lds_dst, const char* base, unsi
 }
 #pragma clang diagnostic pop
 
+// A split-KV schedule's split rows: split[j] = {row, first part, parts}, in
+// increasing row order; part k of row j is o_part / lse_part row first + k.
+struct SplitRows {
+  const float* o_part;
+  const float* lse_part;
+  const int* split;
+  int n_split;
+  float* lse;
+};
+
+// Split entry {first part, parts} of row t, or parts = 0 if row t is not
+// split; tw (uniform) is the first of the 16 rows this wave loads,
+// t = tw + (lane & 15).  A 64-way search finds the first entry with row >= tw
+// (one round per factor of 64 entries); rows are distinct, so the wave's
+// split rows are among the 16 entries from there.
+struct SplitEntry {
+  int first, parts;
+};
+__device__ __forceinline__ SplitEntry split_entry(const int* __restrict__ split, int n_split,
+                                                  int tw, int t) {
+  const int lane = lane_id();
+  int lo = 0, len = n_split;   // the answer is lo + #{entries in [lo, lo + len) below tw}
+  while (len > 0) {
+    const int step = (len + 63) >> 6;
+    const int off = lane * step;
+    const bool below = off < len && split[3 * (lo + off)] < tw;
+    const int c = __popcll(__ballot(below));   // samples are sorted: a prefix is below
+    if (c == 0) break;
+    const int nlo = lo + (c - 1) * step + 1;
+    len = min(lo + c * step, lo + len) - nlo;
+    lo = nlo;
+  }
+  const int j = lo + (lane & 15);
+  int row_j = -1, first_j = 0, parts_j = 0;
+  if (j < n_split) {
+    row_j = split[3 * j];
+    first_j = split[3 * j + 1];
+    parts_j = split[3 * j + 2];
+  }
+  SplitEntry e{0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (__builtin_amdgcn_readlane(row_j, i) == t)
+      e = SplitEntry{__builtin_amdgcn_readlane(first_j, i), __builtin_amdgcn_readlane(parts_j, i)};
+  return e;
+}
+
 // Workgroup (h, y) runs row chunks y, y + gridDim.y, ... of head h against
-// one staged copy of W^UV_h.
+// one staged copy of W^UV_h.  PLANNED: rows listed in sp are merged from
+// their partial outputs (and their log-sum-exp written to sp.lse); the other
+// rows are read from o_lat.
+template <bool PLANNED>
 __global__ void __launch_bounds__(256) out_proj_bf16_kernel(const float* __restrict__ o_lat,
                                                             const uint16_t* __restrict__ w_uv,
-                                                            int T, int n_h, float* __restrict__ out) {
+                                                            int T, int n_h, float* __restrict__ out,
+                                                            SplitRows sp) {
   __shared__ __attribute__((aligned(16))) char wl[D_H * WPITCH];   // [128][WPITCH]
   const int h = blockIdx.x;
   const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
@@ -90,7 +146,7 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(const float* __restr
   // 16 k-steps), loaded whole: one workgroup fits a CU, so registers are
   // plentiful, and the first chunk's loads land while W^UV is staged.
   float4 raw[D_C / 32][2];
-  auto load_rows = [&](int t) {
+  auto load_plain = [&](int t) __attribute__((always_inline)) {
     const bool ok = t < T;
     const float4* lrow = reinterpret_cast<const float4*>(o_lat + ((long)t * n_h + h) * D_C + 8 * g);
 #pragma unroll
@@ -99,20 +155,123 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(const float* __restr
       raw[ks][1] = ok ? lrow[ks * 8 + 1] : float4{0, 0, 0, 0};
     }
   };
-  load_rows(blockIdx.y * TCH + wave * 16 + r16);
-
+  // Split row: o = sum_k exp(lse_k - LSE) o_k with LSE = log sum_k exp(lse_k);
+  // parts with lse_k = -inf weigh nothing, and a row whose parts are all
+  // empty gets o = 0, LSE = -inf.  Registers hold the row and half of one
+  // more part: the first four lse_k, part 0 (or the o_lat row of a row that
+  // is not split) and the first half of part 1 are loaded together, then one
+  // half part at a time.
+  float4 tmp[D_C / 64][2];
+  auto load_merged = [&](int t) __attribute__((always_inline)) {
+    const int tw = __builtin_amdgcn_readfirstlane(t - r16);
+    const SplitEntry se = tw < T ? split_entry(sp.split, sp.n_split, tw, t) : SplitEntry{0, 0};
+    const bool merged = se.parts > 0;
+    const int parts = merged ? se.parts : (t < T ? 1 : 0);
+    const long pstride = (long)n_h * D_C;   // floats between consecutive parts
+    const float* p0 = (merged ? sp.o_part + ((long)se.first * n_h + h) * D_C
+                              : o_lat + ((long)t * n_h + h) * D_C) + 8 * g;
+    const float* l0 = sp.lse_part + (long)se.first * n_h + h;
+    float l[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) l[k] = merged && k < parts ? l0[(long)k * n_h] : -INFINITY;
+#pragma unroll
+    for (int ks = 0; ks < D_C / 32; ++ks) {
+      const float4* src = reinterpret_cast<const float4*>(p0 + ks * 32);
+      raw[ks][0] = parts > 0 ? src[0] : float4{0, 0, 0, 0};
+      raw[ks][1] = parts > 0 ? src[1] : float4{0, 0, 0, 0};
+    }
+    auto load_half = [&](int k, int half) __attribute__((always_inline)) {
+      const float* pk = p0 + k * pstride + half * (D_C / 2);
+#pragma unroll
+      for (int i = 0; i < D_C / 64; ++i) {
+        const float4* src = reinterpret_cast<const float4*>(pk + i * 32);
+        tmp[i][0] = k < parts ? src[0] : float4{0, 0, 0, 0};
+        tmp[i][1] = k < parts ? src[1] : float4{0, 0, 0, 0};
+      }
+    };
+    load_half(1, 0);
+    if (!merged) return;
+    float m = -INFINITY, z = 0.0f;   // running max and sum of exp(lse_k - m)
+    auto add_lse = [&](float lk) __attribute__((always_inline)) {
+      if (lk == -INFINITY) return;
+      if (lk > m) {
+        z = z * __expf(m - lk) + 1.0f;
+        m = lk;
+      } else {
+        z += __expf(lk - m);
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < 4; ++k) add_lse(l[k]);
+    for (int k = 4; k < parts; ++k) add_lse(l0[(long)k * n_h]);
+    const float inv = z > 0.0f ? 1.0f / z : 0.0f;
+    auto weight = [&](int k) __attribute__((always_inline)) {
+      const float lk = k == 0 ? l[0] : k == 1 ? l[1] : k == 2 ? l[2] : k == 3 ? l[3]
+                                                                       : l0[(long)k * n_h];
+      return lk == -INFINITY ? 0.0f : __expf(lk - m) * inv;
+    };
+    const float w0 = weight(0);
+    if (w0 == 0.0f) {
+#pragma unroll
+      for (int ks = 0; ks < D_C / 32; ++ks) raw[ks][0] = raw[ks][1] = float4{0, 0, 0, 0};
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < D_C / 32; ++ks)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          raw[ks][q].x *= w0;
+          raw[ks][q].y *= w0;
+          raw[ks][q].z *= w0;
+          raw[ks][q].w *= w0;
+        }
+    }
+    for (int k = 1; k < parts; ++k) {
+      const float w = weight(k);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (half == 1 || k > 1) load_half(k, half);
+        if (w != 0.0f) {
+#pragma unroll
+          for (int i = 0; i < D_C / 64; ++i)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              float4& r = raw[half * (D_C / 64) + i][q];
+              r.x += w * tmp[i][q].x;
+              r.y += w * tmp[i][q].y;
+              r.z += w * tmp[i][q].z;
+              r.w += w * tmp[i][q].w;
+            }
+        }
+      }
+    }
+    if (sp.lse != nullptr && g == 0) sp.lse[(long)t * n_h + h] = z > 0.0f ? m + __logf(z) : -INFINITY;
+  };
+  auto load_rows = [&](int t) __attribute__((always_inline)) {
+    if constexpr (PLANNED)
+      load_merged(t);
+    else
+      load_plain(t);
+  };
   // stage W^UV_h with direct-to-LDS loads, all in flight at once: one
   // 64-lane instruction moves one 1024-byte row into its padded LDS row;
   // wave w moves rows w, w + 4, ...
-  {
+  auto stage_w = [&]() __attribute__((always_inline)) {
     const char* wh = reinterpret_cast<const char*>(w_uv + (long)h * D_H * D_C);
     const unsigned wl_base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)wl;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll 8
     for (int r = wave_u; r < D_H; r += 4)
       dma_row(wl_base + r * WPITCH, wh + (long)r * D_C * 2, lane * 16);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's rows (and o_lat loads) landed
+  };
+  // the merged rows take a few dependent loads: start the weights first
+  if constexpr (PLANNED) {
+    stage_w();
+    load_rows(blockIdx.y * TCH + wave * 16 + r16);
+  } else {
+    load_rows(blockIdx.y * TCH + wave * 16 + r16);
+    stage_w();
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's rows (and o_lat loads) landed
   __syncthreads();
 
   for (int t0 = blockIdx.y * TCH; t0 < T; t0 += gridDim.y * TCH) {
@@ -202,11 +361,31 @@ hipError_t launch_out_proj(const float* o_lat, const void* w_uv, int T, int n_h,
     // once for all of its chunks
     const int chunks = (T + TCH - 1) / TCH;
     const int per_wg = max(1, (chunks * n_h + 511) / 512);
-    hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(n_h, (chunks + per_wg - 1) / per_wg), block, 0,
-                       stream, o_lat, (const uint16_t*)w_uv, T, n_h, out);
+    hipLaunchKernelGGL(out_proj_bf16_kernel<false>, dim3(n_h, (chunks + per_wg - 1) / per_wg),
+                       block, 0, stream, o_lat, (const uint16_t*)w_uv, T, n_h, out, SplitRows{});
   } else
     hipLaunchKernelGGL(out_proj_kernel<F32>, grid, block, 0, stream, o_lat, (const float*)w_uv, T,
                        n_h, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_out_proj_planned(float* o_lat, const float* o_part, const float* lse_part,
+                                   const int* split, int n_split, const void* w_uv, int T, int n_h,
+                                   int dtype, float* out, float* lse, hipStream_t stream) {
+  if (dtype != 1 || n_split == 0) {
+    // fp32 weights: merge into o_lat, then the plain projection
+    if (n_split > 0) {
+      const hipError_t st =
+          launch_combine_planned(o_part, lse_part, split, n_split, n_h, o_lat, lse, stream);
+      if (st != hipSuccess) return st;
+    }
+    return launch_out_proj(o_lat, w_uv, T, n_h, dtype, out, stream);
+  }
+  const int chunks = (T + TCH - 1) / TCH;
+  const int per_wg = max(1, (chunks * n_h + 511) / 512);
+  hipLaunchKernelGGL(out_proj_bf16_kernel<true>, dim3(n_h, (chunks + per_wg - 1) / per_wg), dim3(256),
+                     0, stream, o_lat, (const uint16_t*)w_uv, T, n_h, out,
+                     SplitRows{o_part, lse_part, split, n_split, lse});
   return hipGetLastError();
 }
 

@@ -157,22 +157,33 @@ def upload(prob: Problem, num_splits: Optional[int] = None, device="cuda",
 
 
 def step(dp: DeviceProblem, stream=None):
-    """One pass of the hot path: append -> absorb -> decode -> combine -> out-proj."""
+    """One pass of the hot path: append -> absorb -> decode -> combine -> out-proj.
+    Under a balanced plan the combine runs inside the out-projection's loads
+    (dp.o_lat then holds only the rows the plan did not split)."""
     mla.mla_kv_append(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r, dp.new_seq,
                       dp.new_pos, ROPE_BASE, stream=stream)
     mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE, stream=stream)
-    decode(dp, stream=stream)
-    mla.mla_out_proj(dp.o_lat, dp.w_uv, dp.out, stream=stream)
+    if dp.num_splits == 0:
+        _attend_planned(dp, stream)
+        mla.mla_out_proj_planned(dp.o_lat, dp.o_part, dp.lse_part, dp.split, dp.w_uv, dp.out,
+                                 dp.lse, stream=stream)
+    else:
+        decode(dp, stream=stream)
+        mla.mla_out_proj(dp.o_lat, dp.w_uv, dp.out, stream=stream)
+
+
+def _attend_planned(dp: DeviceProblem, stream=None):
+    mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
+                                 softmax_scale(), dp.work, dp.o_lat, dp.lse,
+                                 o_part=dp.o_part, lse_part=dp.lse_part, lists=dp.lists,
+                                 stream=stream)
 
 
 def decode(dp: DeviceProblem, stream=None):
     """Attention over the cache (+ split merge) into dp.o_lat / dp.lse."""
     S = dp.num_splits
     if S == 0:
-        mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
-                                     softmax_scale(), dp.work, dp.o_lat, dp.lse,
-                                     o_part=dp.o_part, lse_part=dp.lse_part, lists=dp.lists,
-                                     stream=stream)
+        _attend_planned(dp, stream)
         if dp.split.shape[0] > 0:
             mla.mla_combine_planned(dp.o_part, dp.lse_part, dp.split, dp.n_h, dp.o_lat, dp.lse,
                                     stream=stream)

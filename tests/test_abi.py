@@ -86,6 +86,15 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert lib.mla_out_proj(FAKE, FAKE, 4, 16, 3, FAKE, None) == 4
     assert lib.mla_out_proj(NULL, FAKE, 4, 16, 1, FAKE, None) == 1
     assert lib.mla_out_proj(NULL, NULL, 0, 16, 1, NULL, None) == 0
+    op = lib.mla_out_proj_planned
+    assert op(FAKE, FAKE, FAKE, FAKE, 2, FAKE, 4, 16, 3, FAKE, FAKE, None) == 4   # dtype
+    assert op(FAKE, FAKE, FAKE, FAKE, 5, FAKE, 4, 16, 1, FAKE, FAKE, None) == 2   # n_split > T
+    assert op(FAKE, FAKE, FAKE, FAKE, -1, FAKE, 4, 16, 1, FAKE, FAKE, None) == 2
+    assert op(FAKE, FAKE, FAKE, NULL, 2, FAKE, 4, 16, 1, FAKE, FAKE, None) == 1   # split
+    assert op(FAKE, NULL, FAKE, FAKE, 2, FAKE, 4, 16, 1, FAKE, FAKE, None) == 1   # o_part
+    assert op(FAKE, FAKE, FAKE, FAKE, 2, FAKE, 4, 16, 1, MISALIGNED, FAKE, None) == 3
+    assert op(FAKE, MISALIGNED, FAKE, FAKE, 2, FAKE, 4, 16, 1, FAKE, FAKE, None) == 3
+    assert op(NULL, NULL, NULL, NULL, 0, NULL, 0, 16, 1, NULL, NULL, None) == 0  # T == 0
 
 
 def test_split_plan_matches_oracle_rule():

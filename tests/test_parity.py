@@ -240,6 +240,66 @@ def test_out_proj_matches_oracle(dtype):
     assert rel_err(out.cpu().numpy(), ref) <= (1e-5 if dtype == "f32" else 1e-4)
 
 
+# (T, n_h, weight dtype, fraction of rows split): several row chunks and
+# waves, a wave with split and unsplit rows, more split rows than one 64-way
+# search round covers, every row split, and no split row.
+PLANNED_PROJ = [(300, 16, "bf16", 0.6), (2560, 16, "bf16", 0.6), (130, 32, "bf16", 1.0),
+                (300, 16, "f32", 0.6), (70, 16, "bf16", 0.0)]
+
+
+@pytest.mark.parametrize("T,n_h,dtype,frac", PLANNED_PROJ,
+                         ids=[f"T{c[0]}-h{c[1]}-{c[2]}-{c[3]}" for c in PLANNED_PROJ])
+def test_out_proj_planned_merges_split_rows(T, n_h, dtype, frac):
+    """Merge-and-project against the oracle's log-sum-exp merge followed by its
+    projection.  Parts of weight zero (lse = -inf) hold NaN and the o_lat rows
+    of split rows hold NaN: neither may reach the output."""
+    import torch
+    from mla_latent_kv_04_amd import _binding as mla
+    rng = np.random.default_rng(12)
+    rows = np.sort(rng.choice(T, size=int(frac * T), replace=False)).astype(np.int32)
+    counts = rng.integers(2, 7, size=len(rows)).astype(np.int32)
+    if len(rows) > 5:
+        counts[5] = 9                      # more parts than the first batch of lse loads
+    first = (np.cumsum(counts) - counts).astype(np.int32)
+    n_parts = int(counts.sum())
+    o_part = rng.standard_normal((n_parts, n_h, D_C)).astype(np.float32)
+    lse_part = (rng.standard_normal((n_parts, n_h)) * 4).astype(np.float32)
+    lse_part[rng.random((n_parts, n_h)) < 0.15] = -np.inf
+    if len(rows) > 3:
+        lse_part[first[3]:first[3] + counts[3], 2] = -np.inf   # a row whose parts are all empty
+    o_part[np.isneginf(lse_part)] = 0.0
+    o_lat = rng.standard_normal((T, n_h, D_C)).astype(np.float32)
+    w = (rng.standard_normal((n_h, 128, D_C)) / math.sqrt(D_C)).astype(np.float32)
+    if dtype == "bf16":
+        w = round_to_bf16(w)
+    merged = o_lat.astype(np.float64)
+    lref = np.full((T, n_h), 7.0)
+    for j, r in enumerate(rows):
+        sl = slice(first[j], first[j] + counts[j])
+        merged[r], lref[r] = orc.combine_splits(o_part[sl], lse_part[sl])
+    ref = orc.out_projection(merged, w)
+
+    say(f"out_proj_planned T={T} n_h={n_h} {dtype} frac={frac}")
+    poisoned = o_part.copy()
+    poisoned[np.isneginf(lse_part)] = np.nan
+    lat = o_lat.copy()
+    lat[rows] = np.nan
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    split = np.stack([rows, first, counts], axis=1).astype(np.int32).reshape(-1, 3)
+    out = torch.empty((T, n_h, 128), device="cuda")
+    lse = torch.full((T, n_h), 7.0, device="cuda")
+    mla.mla_out_proj_planned(torch.from_numpy(lat).cuda(),
+                             torch.from_numpy(poisoned).cuda(),
+                             torch.from_numpy(lse_part).cuda(), torch.from_numpy(split).cuda(),
+                             torch.from_numpy(w).to(tdt).cuda(), out, lse)
+    torch.cuda.synchronize()
+    assert rel_err(out.cpu().numpy(), ref) <= (1e-5 if dtype == "f32" else 1e-4)
+    got_l = lse.cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(np.isneginf(got_l), np.isneginf(lref))
+    fin = np.isfinite(lref)
+    np.testing.assert_allclose(got_l[fin], lref[fin], rtol=1e-6, atol=1e-5)
+
+
 def test_block_permutation_gives_identical_bits():
     """The same logical cache under two different block tables: bitwise equal."""
     a = small(F3, B=3, ctx=[300, 64, 191], seed=77)
