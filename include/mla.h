@@ -65,6 +65,8 @@ extern "C" {
 #define MLA_D_H 128
 #define MLA_ROW 576
 #define MLA_BLOCK 64
+/* Segment cost of mla_plan_decode's schedule, in blocks. */
+#define MLA_PLAN_SEGMENT_COST 8
 
 enum mla_dtype { MLA_F32 = 0, MLA_BF16 = 1 };
 
@@ -207,13 +209,21 @@ int32_t mla_split_plan(const int32_t* seq_lens, int32_t B, int32_t block_size, i
  * blocks.  Lay the rows' blocks end to end (row 0 first): row r occupies
  * positions [S_r, S_r + T_r) of a sequence of N = sum_r T_r blocks.  With
  * G = n_h / 64 workgroups per unit of work when n_h is a multiple of 64 (else
- * G = 1), K = max(1, min(floor(num_slots / G), N)) lists (K = 1 when N = 0),
- * list k owns positions [floor(k N / K), floor((k+1) N / K)): equal shares to
- * within one block, so that K * G workgroups finish together.  A row whose
- * blocks fall in lists k0..k1 is cut at the list boundaries into k1 - k0 + 1
- * segments; a row with no block is one empty segment in the list owning
- * position S_r (the last list if S_r = N).  Segment keys are
- * [64 t0, min(64 t1, n_r)) for its blocks [t0, t1) of the row.
+ * G = 1), K = max(1, min(floor(num_slots / G), N)) lists (K = 1 when N = 0)
+ * cover the positions in order, list k owning [b_k, b_{k+1}).  A list costs its
+ * blocks plus C = MLA_PLAN_SEGMENT_COST per segment (the fixed price of
+ * starting a row: its query, the first tiles, its output).  The boundaries
+ * come from a greedy walk with capacity W: a list starts where the previous
+ * one ended and takes the rest of the current row while its cost stays
+ * <= W; the first rest that does not fit is cut after W - cost - C blocks when
+ * that is >= 1, and the list closes.  W is the least capacity for which the
+ * walk needs at most K lists (so the costliest list is as cheap as any
+ * partition into K ordered lists allows); lists past the last one the walk
+ * fills are empty (b_k = N).  A row whose blocks fall in lists k0..k1 is cut
+ * at the list boundaries into k1 - k0 + 1 segments; a row with no block is one
+ * empty segment in the last list with b_k <= S_r (the last list if S_r = N).
+ * Segment keys are [64 t0, min(64 t1, n_r)) for its blocks [t0, t1) of the
+ * row.
  *
  *   work  (host out, int32 [n_work, 4]) = {row, key_begin, key_end, slot},
  *         ordered by list, then row; slot = -1 for a row in one segment (its

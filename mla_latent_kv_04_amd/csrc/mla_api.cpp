@@ -123,13 +123,42 @@ int32_t mla_plan_decode(const int32_t* seq_lens, int32_t B, int32_t q_len, int32
   }
   const int64_t groups = (n_h % 64 == 0) ? n_h / 64 : 1;
   const int64_t K = total > 0 ? std::max<int64_t>(1, std::min<int64_t>(num_slots / groups, total)) : 1;
-  // list k covers concatenated blocks [bound(k), bound(k + 1))
-  auto bound = [&](int64_t k) { return k * total / K; };
-  auto list_of = [&](int64_t pos) {  // the list whose range holds block pos (pos < total)
-    int64_t k = pos * K / std::max<int64_t>(total, 1);
-    while (k + 1 < K && bound(k + 1) <= pos) ++k;
-    while (k > 0 && bound(k) > pos) --k;
-    return k;
+  // List capacity W: the least for which the greedy walk below fills at most
+  // K lists, where a list's cost is its blocks plus C per segment.
+  const int64_t C = MLA_PLAN_SEGMENT_COST;
+  auto walk = [&](int64_t W, std::vector<int64_t>* starts) {
+    int64_t used = 0, pos = 0, r = 0;
+    while (pos < total) {
+      if (starts) starts->push_back(pos);
+      if (++used > K && !starts) return used;
+      int64_t cost = 0;
+      while (pos < total) {
+        while (start[r] + tiles[r] <= pos) ++r;   // the row holding block pos
+        const int64_t rest = start[r] + tiles[r] - pos;
+        if (cost + C + rest <= W) {
+          cost += C + rest;
+          pos += rest;
+          continue;
+        }
+        if (W - cost - C >= 1) pos += W - cost - C;
+        break;
+      }
+    }
+    return used;
+  };
+  int64_t lo = C + 1, hi = C + 1;
+  for (int64_t r = 0; r < rows; ++r) hi += tiles[r] > 0 ? C + tiles[r] : 0;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (walk(mid, nullptr) <= K) hi = mid; else lo = mid + 1;
+  }
+  // list k covers concatenated blocks [bnd[k], bnd[k + 1]); unused lists are empty
+  std::vector<int64_t> bnd;
+  if (total > 0) walk(lo, &bnd);
+  bnd.resize(K + 1, total);
+  auto bound = [&](int64_t k) { return bnd[k]; };
+  auto list_of = [&](int64_t pos) {  // the last list starting at or before block pos (pos < total)
+    return (int64_t)(std::upper_bound(bnd.begin(), bnd.begin() + K, pos) - bnd.begin()) - 1;
   };
   struct Seg { int64_t list, row, kb, ke, slot; };
   std::vector<Seg> segs;

@@ -8,19 +8,57 @@ import pytest
 from mla_latent_kv_04_amd import _binding as B
 
 
-def python_plan(seq_lens, q_len, n_h, slots, bs=64):
-    """Restatement of the schedule's definition (include/mla.h)."""
+SEG_COST = 8   # MLA_PLAN_SEGMENT_COST
+
+
+def _row_blocks(seq_lens, q_len, bs=64):
     rows = []
     for L in seq_lens:
         L = max(0, int(L))
         for m in range(q_len):
             rows.append(max(0, min(L, L - (q_len - 1 - m))))
-    tiles = [(n + bs - 1) // bs for n in rows]
+    return rows, [(n + bs - 1) // bs for n in rows]
+
+
+def greedy_starts(tiles, W, C=SEG_COST):
+    """List start positions of the greedy walk with capacity W (include/mla.h)."""
+    pieces = [t for t in tiles if t > 0]
+    starts, pos, i, off = [], 0, 0, 0
+    while i < len(pieces):
+        starts.append(pos)
+        cost = 0
+        while i < len(pieces):
+            rest = pieces[i] - off
+            if cost + C + rest <= W:
+                cost += C + rest
+                pos += rest
+                i, off = i + 1, 0
+            else:
+                if W - cost - C >= 1:
+                    off += W - cost - C
+                    pos += W - cost - C
+                break
+    return starts
+
+
+def python_plan(seq_lens, q_len, n_h, slots, bs=64):
+    """Restatement of the schedule's definition (include/mla.h)."""
+    rows, tiles = _row_blocks(seq_lens, q_len, bs)
     starts = list(np.cumsum([0] + tiles[:-1])) if tiles else []
     N = sum(tiles)
     G = n_h // 64 if n_h % 64 == 0 else 1
     K = max(1, min(slots // G, N)) if N > 0 else 1
-    bounds = [k * N // K for k in range(K + 1)]
+    W = SEG_COST + 1
+    if N > 0:
+        hi = SEG_COST + 1 + sum(SEG_COST + t for t in tiles if t > 0)
+        while W < hi:
+            mid = (W + hi) // 2
+            if len(greedy_starts(tiles, mid)) <= K:
+                hi = mid
+            else:
+                W = mid + 1
+    bounds = (greedy_starts(tiles, W) if N > 0 else []) + [N] * (K + 1)
+    bounds = bounds[:K + 1]
 
     def owner(pos):
         if pos >= N:
@@ -96,6 +134,15 @@ def test_plan_covers_every_row_exactly_once(lens, q_len, n_h, slots):
         assert count == len(covered[row]) > 1
 
 
+def _list_costs(work, lists):
+    costs = []
+    for k in range(len(lists) - 1):
+        items = work[lists[k]:lists[k + 1]]
+        blk = [(ke + 63) // 64 - kb // 64 for _, kb, ke, _ in items.tolist() if ke > kb]
+        costs.append(sum(blk) + SEG_COST * len(blk))
+    return costs
+
+
 @pytest.mark.parametrize("lens,q_len,n_h,slots", CASES)
 def test_plan_lists_are_balanced(lens, q_len, n_h, slots):
     work, lists, split, n_parts = B.mla_plan_decode(lens, q_len, n_h, slots)
@@ -103,14 +150,27 @@ def test_plan_lists_are_balanced(lens, q_len, n_h, slots):
     K = len(lists) - 1
     assert 1 <= K <= max(1, slots // G) and lists[0] == 0 and lists[-1] == len(work)
     assert np.all(np.diff(lists) >= 0)
-    blocks = []
     for k in range(K):
-        items = work[lists[k]:lists[k + 1]]
-        rows_k = items[:, 0].tolist()
+        rows_k = work[lists[k]:lists[k + 1], 0].tolist()
         assert rows_k == sorted(rows_k) and len(set(rows_k)) == len(rows_k)
-        blocks.append(int(sum((ke + 63) // 64 - kb // 64 for _, kb, ke, _ in items.tolist())))
-    if sum(blocks) > 0:
-        assert max(blocks) - min(blocks) <= 1
+    costs = _list_costs(work, lists)
+    W = max(costs)
+    if W == 0:
+        return
+    _, tiles = _row_blocks(lens, q_len)
+    N = sum(tiles)
+    # no partition into K ordered lists is cheaper: one unit less of capacity
+    # needs more than K lists
+    if W > SEG_COST + 1:
+        assert len(greedy_starts(tiles, W - 1)) > K
+    # and never costlier than equal block shares (the plain split)
+    eq = [k * N // K for k in range(K + 1)]
+    starts = np.cumsum([0] + tiles[:-1])
+    eq_costs = []
+    for k in range(K):
+        segs = [(s, t) for s, t in zip(starts, tiles) if t > 0 and s < eq[k + 1] and s + t > eq[k]]
+        eq_costs.append(eq[k + 1] - eq[k] + SEG_COST * len(segs))
+    assert W <= max(eq_costs)
 
 
 def test_plan_reports_required_capacity():
