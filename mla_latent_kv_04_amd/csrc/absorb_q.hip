@@ -18,6 +18,8 @@
 // stores (four lanes cover a row's 64 columns).  The RoPE half of q_lat is
 // shared out over the eight column-chunk workgroups of a head, 4 of the 32
 // rotation pairs each.
+#include <cmath>
+
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -26,7 +28,14 @@ namespace mla {
 namespace {
 
 constexpr int CCH = 64;        // latent columns per workgroup
+
+// RoPE frequencies in revolutions per position, theta_k / (2 pi) with
+// theta_k = base^(-2k / d_R), computed on the host in float64.
+struct RopeRev {
+  double r[D_R / 2];
+};
 constexpr int TCH = 128;       // rows per workgroup (4 waves x 2 blocks of 16)
+constexpr int KPW = (D_R / 2) / (D_C / CCH);   // RoPE pairs per workgroup
 
 template <class E> struct AbsorbLds;
 // bf16: a 136-byte row pitch puts the four rows of a transposing read on
@@ -88,7 +97,7 @@ template <class E>
 __global__ void __launch_bounds__(256) absorb_q_kernel(
     const typename E::storage* __restrict__ q_nope, const typename E::storage* __restrict__ q_rope,
     const typename E::storage* __restrict__ w_uk, const int* __restrict__ q_pos, int T, int n_h,
-    double base, typename E::storage* __restrict__ q_lat) {
+    double base, RopeRev rev, typename E::storage* __restrict__ q_lat) {
   using T_ = typename E::storage;
   constexpr int S = AbsorbLds<E>::stride;
   __shared__ __attribute__((aligned(16))) char lds[D_H * S];
@@ -113,6 +122,25 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
       }
     }
   }
+  // bf16 RoPE inputs (two rotation pairs per thread), loaded with the
+  // fragments and rotated after the product, so their latency is hidden
+  constexpr int RPT = TCH * KPW / 256;
+  static_assert(TCH * KPW % 256 == 0, "rotation pairs split evenly");
+  uint32_t rp[RPT];
+  int rpos[RPT];
+  if constexpr (E::bytes == 2) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      const int t = t0 + e / KPW, k = blockIdx.y * KPW + e % KPW;
+      rp[i] = 0;
+      rpos[i] = 0;
+      if (t < T) {
+        rp[i] = *reinterpret_cast<const uint32_t*>(q_rope + ((long)t * n_h + h) * D_R + 2 * k);
+        rpos[i] = q_pos[t];
+      }
+    }
+  }
   // Stage W^UK_h[0:128, c0:c0+64] (16-byte pieces, written as two halves:
   // the bf16 row pitch is a multiple of 8 bytes only).
   constexpr int PER16 = 16 / E::bytes;
@@ -127,18 +155,17 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
     wv[i] = *reinterpret_cast<const uint4*>(wsrc + (long)d * D_C + q * PER16);
   }
 
-  // Decoupled RoPE query, this column chunk's 4 of the 32 rotation pairs (its
-  // float64 angle arithmetic runs while the loads above are in flight).
-  {
-    constexpr int KPW = (D_R / 2) / (D_C / CCH);  // pairs per workgroup
+  // Decoupled RoPE query, this column chunk's 4 of the 32 rotation pairs.
+  if constexpr (E::bytes == 4) {
+    // fp32: float64 angles and rotation (runs while the loads above are in flight)
     for (int e = threadIdx.x; e < TCH * KPW; e += 256) {
       const int t = t0 + e / KPW, k = blockIdx.y * KPW + e % KPW;
       if (t >= T) break;
+      const T_* src = q_rope + ((long)t * n_h + h) * D_R;
+      T_* dst = q_lat + ((long)t * n_h + h) * ROW + D_C;
       double c, s;
       rope_cs(q_pos[t], k, base, c, s);
-      const T_* src = q_rope + ((long)t * n_h + h) * D_R;
       double x = E::to_f32(src[2 * k]), y = E::to_f32(src[2 * k + 1]);
-      T_* dst = q_lat + ((long)t * n_h + h) * ROW + D_C;
       dst[2 * k] = E::from_f32((float)(x * c - y * s));
       dst[2 * k + 1] = E::from_f32((float)(x * s + y * c));
     }
@@ -179,6 +206,23 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
       store16<E>(q_lat + ((long)t * n_h + h) * ROW + c0 + 16 * g, v);
     }
   }
+  if constexpr (E::bytes == 2) {
+    // the angle is reduced exactly in float64 (whole turns dropped), then sine
+    // and cosine in float32, far below bf16's rounding
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      const int t = t0 + e / KPW, k = blockIdx.y * KPW + e % KPW;
+      if (t >= T) continue;
+      double turns = (double)rpos[i] * rev.r[k];
+      turns -= rint(turns);
+      float sf, cf;
+      sincosf((float)(turns * 6.283185307179586), &sf, &cf);
+      const float x = bf16_to_f32((uint16_t)(rp[i] & 0xFFFFu)), y = bf16_to_f32((uint16_t)(rp[i] >> 16));
+      *reinterpret_cast<uint32_t*>(q_lat + ((long)t * n_h + h) * ROW + D_C + 2 * k) =
+          pack_bf16x2(x * cf - y * sf, x * sf + y * cf);
+    }
+  }
 
 }
 
@@ -188,13 +232,16 @@ hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w
                            const int* q_pos, int T, int n_h, int dtype, float base, void* q_lat,
                            hipStream_t stream) {
   dim3 grid(n_h, D_C / CCH, (T + TCH - 1) / TCH), block(256);
+  RopeRev rev;
+  for (int k = 0; k < D_R / 2; ++k)
+    rev.r[k] = std::pow((double)base, -(double)(2 * k) / (double)D_R) / 6.283185307179586;
   if (dtype == 1)
     hipLaunchKernelGGL(absorb_q_kernel<BF16>, grid, block, 0, stream, (const uint16_t*)q_nope,
                        (const uint16_t*)q_rope, (const uint16_t*)w_uk, q_pos, T, n_h,
-                       (double)base, (uint16_t*)q_lat);
+                       (double)base, rev, (uint16_t*)q_lat);
   else
     hipLaunchKernelGGL(absorb_q_kernel<F32>, grid, block, 0, stream, (const float*)q_nope,
-                       (const float*)q_rope, (const float*)w_uk, q_pos, T, n_h, (double)base,
+                       (const float*)q_rope, (const float*)w_uk, q_pos, T, n_h, (double)base, rev,
                        (float*)q_lat);
   return hipGetLastError();
 }
