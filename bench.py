@@ -123,8 +123,10 @@ def cpu_baseline(prob, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the device needs a few hundred steps (~0.1 s) to settle its clocks and
+    # caches; the timed region is then steady state
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="v2_bf16_B128_L1k-8k")
     ap.add_argument("--splits", type=int, default=None,
                     help="split-KV partitions per row; 0 = balanced work plan (default: workload's)")

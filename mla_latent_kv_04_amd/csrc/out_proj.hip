@@ -263,14 +263,10 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(const float* __restr
     for (int r = wave_u; r < D_H; r += 4)
       dma_row(wl_base + r * WPITCH, wh + (long)r * D_C * 2, lane * 16);
   };
-  // the merged rows take a few dependent loads: start the weights first
-  if constexpr (PLANNED) {
-    stage_w();
-    load_rows(blockIdx.y * TCH + wave * 16 + r16);
-  } else {
-    load_rows(blockIdx.y * TCH + wave * 16 + r16);
-    stage_w();
-  }
+  // (the rows first: with the weights first, measured 2% slower even where
+  // the rows take a few dependent loads)
+  load_rows(blockIdx.y * TCH + wave * 16 + r16);
+  stage_w();
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's rows (and o_lat loads) landed
   __syncthreads();
 
