@@ -64,7 +64,7 @@ class Workload:
 # decode, V2 128K split-KV decode and V2 chunked prefill.
 WORKLOADS = {
     "v2lite_f32_L256": Workload("v2lite_f32_L256", "f32", B=1, n_h=16, ctx=256,
-                                table="identity", seed=1001, num_splits=1),
+                                table="identity", seed=1001),
     "v2lite_bf16_B64_L4096": Workload("v2lite_bf16_B64_L4096", "bf16", B=64, n_h=16,
                                       ctx=4096, seed=1002),
     "v2_bf16_B128_L1k-8k": Workload("v2_bf16_B128_L1k-8k", "bf16", B=128, n_h=128,
