@@ -323,7 +323,8 @@ def mla_combine_planned(o_part, lse_part, split, n_h, o_lat, lse=None, stream=No
 
 def mla_out_proj_planned(o_lat, o_part, lse_part, split, w_uv, out, lse=None, stream=None):
     """Merge a plan's split rows and project every row through W^UV (see mla.h).
-    The split rows of o_lat are scratch."""
+    The split rows of o_lat are scratch; split (and o_part, lse_part) may be
+    None when no row is split."""
     torch = _torch()
     f32 = torch.float32
     dt = _dtype_code(w_uv)
@@ -332,9 +333,9 @@ def mla_out_proj_planned(o_lat, o_part, lse_part, split, w_uv, out, lse=None, st
         raise ValueError("o_lat must be [T, n_h, 512] and w_uv [n_h, 128, 512]")
     if tuple(out.shape) != (T, n_h, D_H):
         raise ValueError("out must be [T, n_h, 128]")
-    if split.dim() != 2 or split.shape[1] != 3:
+    if split is not None and (split.dim() != 2 or split.shape[1] != 3):
         raise ValueError("split must be [n_split, 3]")
-    n_split = int(split.shape[0])
+    n_split = int(split.shape[0]) if split is not None else 0
     st = load().mla_out_proj_planned(
         _dev(o_lat, "o_lat", f32), _dev(o_part, "o_part", f32) if n_split else None,
         _dev(lse_part, "lse_part", f32) if n_split else None,
