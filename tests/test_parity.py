@@ -300,6 +300,43 @@ def test_out_proj_planned_merges_split_rows(T, n_h, dtype, frac):
     np.testing.assert_allclose(got_l[fin], lref[fin], rtol=1e-6, atol=1e-5)
 
 
+# Balanced schedules with few slots, so that lists hold many items and rows
+# are cut into many parts: (workload, batch, context range, q_len, n_h, slots).
+DENSE_PLANS = [(F3, 9, (1, 1500), 1, 128, 5), (F3, 3, (1500, 3000), 1, 64, 5),
+               (F3, 2, (3000, 4000), 1, 128, 16), (F2, 4, (300, 2000), 1, 16, 6),
+               (F5, 1, (700, 700), 24, 128, 6)]
+
+
+@pytest.mark.parametrize("wl,B,ctx,q_len,n_h,slots", DENSE_PLANS,
+                         ids=[f"{c[0]}-B{c[1]}-h{c[4]}-slots{c[5]}" for c in DENSE_PLANS])
+def test_dense_plans_match_oracle(wl, B, ctx, q_len, n_h, slots):
+    """Lists of several items (each item change restarts the tile pipeline),
+    rows cut into several parts and merged in the out-projection."""
+    rng = np.random.default_rng(B * 1000 + slots)
+    lens = rng.integers(ctx[0], ctx[1], size=B, endpoint=True)
+    kw = dict(B=B, ctx=[int(x) for x in lens], n_h=n_h)
+    if q_len > 1:
+        kw["q_len"] = q_len
+    prob = small(wl, **kw)
+    say(f"dense plan {wl} B={B} n_h={n_h} slots={slots}")
+    import torch
+    dp = pipeline.upload(prob, num_splits=0, num_slots=slots)
+    assert dp.split.shape[0] > 0 or int(np.diff(dp.lists.cpu().numpy()).max()) > 1
+    pipeline.step(dp)
+    torch.cuda.synchronize()
+    out, lse = to_np(dp.out), to_np(dp.lse)
+    refs, lrefs = [], []
+    for b in range(prob.wl.B):
+        o, l, _ = oracle_sequence(prob, b)
+        refs.append(o)
+        lrefs.append(l)
+    ref, lref = np.concatenate(refs), np.concatenate(lrefs)
+    assert rel_err(out, ref) <= TOL[prob.wl.dtype]
+    fin = np.isfinite(lref)
+    np.testing.assert_array_equal(np.isfinite(lse), fin)
+    assert np.max(np.abs(lse[fin] - lref[fin])) <= TOL[prob.wl.dtype] * max(1.0, float(np.abs(lref[fin]).max()))
+
+
 def test_block_permutation_gives_identical_bits():
     """The same logical cache under two different block tables: bitwise equal."""
     a = small(F3, B=3, ctx=[300, 64, 191], seed=77)
