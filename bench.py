@@ -137,8 +137,8 @@ def main():
                          "known-size reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the attention shards by sequence or key range; see the design notes).",
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(across GPUs the attention would shard by sequence or key range).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -17,8 +17,7 @@ Sources (page title, section / equation):
     [q^C; q^R], [k^C; k^R]; k^R is cached already rotated; cache holds
     (d_c + d_R) elements per token, d_c = 4 d_h, d_R = d_h / 2).
 
-Readings where the pages are silent or garbled (every one is also listed in the
-design notes):
+Readings where the pages are silent or garbled:
   R1 softmax scale: 1/sqrt(d_h + d_R), the width of the concatenated q.k.
   R2 RoPE: rotate adjacent pairs (x[2k], x[2k+1]) by pos * base^(-2k/d_R),
      angles formed in float64.
