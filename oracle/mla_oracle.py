@@ -29,6 +29,16 @@ Readings where the pages are silent or garbled:
   R6 a query row with no visible key yields o = 0 and lse = -inf.
   R7 W^UK / W^UV are stored [n_h, d_h, d_c]: head i owns rows i*d_h..(i+1)*d_h
      of eq. 10/11's matrices (eq. 4-6 ordering).
+  R8 the extra RMSNorm after the compressed latents (blog §3.1.1 names it and
+     gives no formula) is the standard one, g * x / sqrt(mean(x^2) + eps) over
+     the latent's width, with a learned gain g; it is applied to c^KV before it
+     is cached and to c^Q before its up-projections.
+  R9 the decoupled key comes straight from the hidden state, k^R = W^KR h, and
+     the decoupled query from the compressed query, q^R = W^QR c^Q (blog
+     §2.2.2); both are rotated at the token's position.  Down-projections are
+     stored as written in eq. 9 / 12, [d_out, d_model]; W^UQ and W^QR as
+     [n_h * d_h, d_c'] and [n_h * d_R, d_c'], head i owning rows i*d_h.. and
+     i*d_R.. respectively.
 """
 from __future__ import annotations
 
@@ -37,7 +47,7 @@ import numpy as np
 __all__ = [
     "rope_rotate", "mla_attention_naive", "kv_cache_rows", "absorb_query",
     "latent_attention", "split_ranges", "combine_splits", "out_projection",
-    "visible_keys", "mla_reference_problem",
+    "visible_keys", "mla_reference_problem", "rms_norm", "kv_produce", "q_produce",
 ]
 
 F64 = np.float64
@@ -266,3 +276,41 @@ def mla_reference_problem(seq_c_kv, seq_k_r, q_nope, q_rope, w_uk, w_uv, seq_len
     return mla_attention_naive(seq_c_kv[:L], seq_k_r[:L], q_nope, q_rope, w_uk, w_uv,
                                np.arange(L), np.asarray(q_pos), visible_keys(L, q_len),
                                scale, base)
+
+
+# ---------------------------------------------------------------- producers
+def rms_norm(x, gain, eps: float):
+    """The latent RMSNorm (reading R8) over the last axis of x."""
+    x = np.asarray(x, F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return np.asarray(gain, F64) * x / np.sqrt(ms + float(eps))
+
+
+def kv_produce(h, w_dkv, kv_gain, w_kr, pos, base: float, eps: float):
+    """Cache rows of new tokens from their hidden states h [T, d_model].
+
+    c^KV_t = RMSNorm(W^DKV h_t)          (notes §2.1.2 eq. 9, blog §3.1.1; R8)
+    k^R_t  = W^KR h_t, rotated at pos_t  (blog §2.2.2; R9)
+    Returns (c_kv [T, d_c], k_r [T, d_R] before rotation, rows [T, d_c + d_R]),
+    rows being what kv_cache_rows caches for them.
+    """
+    h = np.asarray(h, F64)
+    c_kv = rms_norm(h @ np.asarray(w_dkv, F64).T, kv_gain, eps)
+    k_r = h @ np.asarray(w_kr, F64).T
+    return c_kv, k_r, kv_cache_rows(c_kv, k_r, pos, base)
+
+
+def q_produce(h, w_dq, q_gain, w_uq, w_qr, n_h: int, eps: float):
+    """Per-head queries of tokens h [T, d_model] through the compressed query.
+
+    c^Q_t = RMSNorm(W^DQ h_t)    (notes §2.1.2 eq. 12, blog §3.1.1; R8)
+    q^C_t = W^UQ c^Q_t           (eq. 13), split into heads of d_h
+    q^R_t = W^QR c^Q_t           (blog §2.2.2; R9), before rotation
+    Returns (c_q [T, d_c'], q_nope [T, n_h, d_h], q_rope [T, n_h, d_R]).
+    """
+    h = np.asarray(h, F64)
+    c_q = rms_norm(h @ np.asarray(w_dq, F64).T, q_gain, eps)
+    T = h.shape[0]
+    q_nope = (c_q @ np.asarray(w_uq, F64).T).reshape(T, n_h, -1)
+    q_rope = (c_q @ np.asarray(w_qr, F64).T).reshape(T, n_h, -1)
+    return c_q, q_nope, q_rope

@@ -312,3 +312,76 @@ def test_cached_rows_keep_latent_unrotated():
     rows = orc.kv_cache_rows(c, k, np.arange(5) + 100, 10000.0)
     np.testing.assert_array_equal(rows[:, :8], c)
     np.testing.assert_allclose(rows[:, 8:], orc.rope_rotate(k, np.arange(5) + 100, 1e4))
+
+
+# ---------------------------------------------------------------- producers
+def test_rms_norm_worked_example_and_properties():
+    # [3, 4]: mean square 12.5, root 3.5355..; gain [1, 2]
+    y = orc.rms_norm(np.array([[3.0, 4.0]]), np.array([1.0, 2.0]), 0.0)
+    np.testing.assert_allclose(y, [[3 / np.sqrt(12.5), 8 / np.sqrt(12.5)]], rtol=1e-15)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((7, 512)) * 3.0
+    y = orc.rms_norm(x, np.ones(512), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-13)
+    np.testing.assert_allclose(orc.rms_norm(4.5 * x, np.ones(512), 0.0), y, rtol=1e-13)
+    # eps sits inside the root: an all-zero row stays zero, a tiny row is damped
+    np.testing.assert_array_equal(orc.rms_norm(np.zeros((1, 4)), np.ones(4), 1e-6), 0.0)
+    t = orc.rms_norm(np.full((1, 4), 1e-3), np.ones(4), 1e-6)
+    np.testing.assert_allclose(t, 1e-3 / np.sqrt(1e-6 + 1e-6), rtol=1e-13)
+
+
+def test_kv_produce_identity_weights():
+    """W^DKV = [I 0], W^KR = [0 I]: c^KV is the normalised first d_c features of
+    h and k^R the remaining d_R, rotated in the cached row."""
+    rng = np.random.default_rng(6)
+    d_c, d_r, T = 8, 4, 5
+    h = rng.standard_normal((T, d_c + d_r))
+    w_dkv = np.hstack([np.eye(d_c), np.zeros((d_c, d_r))])
+    w_kr = np.hstack([np.zeros((d_r, d_c)), np.eye(d_r)])
+    pos = np.array([0, 3, 7, 100, 4096])
+    c, k, rows = orc.kv_produce(h, w_dkv, np.ones(d_c), w_kr, pos, 10000.0, 0.0)
+    lat = h[:, :d_c]
+    np.testing.assert_allclose(c, lat / np.sqrt(np.mean(lat * lat, axis=1, keepdims=True)),
+                               rtol=1e-14)
+    np.testing.assert_array_equal(k, h[:, d_c:])
+    np.testing.assert_array_equal(rows[:, :d_c], c)
+    np.testing.assert_allclose(rows[0, d_c:], h[0, d_c:], rtol=1e-15)   # position 0
+    np.testing.assert_allclose(rows[:, d_c:], orc.rope_rotate(h[:, d_c:], pos, 10000.0),
+                               rtol=1e-15)
+
+
+def test_producers_match_scalar_loops():
+    """kv_produce and q_produce against element-by-element sums on tiny,
+    non-square shapes (a transposed weight or a wrong head split fails)."""
+    rng = np.random.default_rng(7)
+    T, d_model, d_c, d_r, d_cq, n_h, d_h = 3, 7, 5, 4, 6, 2, 3
+    h = rng.standard_normal((T, d_model))
+    w_dkv = rng.standard_normal((d_c, d_model))
+    w_kr = rng.standard_normal((d_r, d_model))
+    g_kv = rng.standard_normal(d_c)
+    w_dq = rng.standard_normal((d_cq, d_model))
+    g_q = rng.standard_normal(d_cq)
+    w_uq = rng.standard_normal((n_h * d_h, d_cq))
+    w_qr = rng.standard_normal((n_h * d_r, d_cq))
+    eps = 0.25
+    c, k, _ = orc.kv_produce(h, w_dkv, g_kv, w_kr, np.zeros(T), 10000.0, eps)
+    cq, qn, qr = orc.q_produce(h, w_dq, g_q, w_uq, w_qr, n_h, eps)
+    for t in range(T):
+        lat = [sum(w_dkv[i][j] * h[t][j] for j in range(d_model)) for i in range(d_c)]
+        r = math.sqrt(sum(v * v for v in lat) / d_c + eps)
+        for i in range(d_c):
+            assert abs(c[t][i] - g_kv[i] * lat[i] / r) < 1e-12
+        for i in range(d_r):
+            assert abs(k[t][i] - sum(w_kr[i][j] * h[t][j] for j in range(d_model))) < 1e-12
+        qlat = [sum(w_dq[i][j] * h[t][j] for j in range(d_model)) for i in range(d_cq)]
+        rq = math.sqrt(sum(v * v for v in qlat) / d_cq + eps)
+        cql = [g_q[i] * qlat[i] / rq for i in range(d_cq)]
+        for i in range(d_cq):
+            assert abs(cq[t][i] - cql[i]) < 1e-12
+        for head in range(n_h):
+            for d in range(d_h):
+                want = sum(w_uq[head * d_h + d][j] * cql[j] for j in range(d_cq))
+                assert abs(qn[t][head][d] - want) < 1e-12
+            for d in range(d_r):
+                want = sum(w_qr[head * d_r + d][j] * cql[j] for j in range(d_cq))
+                assert abs(qr[t][head][d] - want) < 1e-12
