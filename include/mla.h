@@ -285,6 +285,53 @@ int32_t mla_out_proj_planned(float* o_lat, const float* o_part, const float* lse
                              const int32_t* split, int32_t n_split, const void* w_uv, int32_t T,
                              int32_t n_h, int32_t dtype, float* out, float* lse, void* stream);
 
+/*
+ * Producers: the projections that feed the path from a layer's hidden states
+ * h [T, d_model] (notes §2.1.2 eq. 9 and 12-13; blog part 2 §2.2.2 for the
+ * decoupled key and query, §3.1.1 for the RMSNorm after the compressed
+ * latents).  The RMSNorm is the standard one over the latent's width:
+ *   RMSNorm(x) = g * x / sqrt(mean(x^2) + eps), g a learned gain (fp32).
+ * Weights are stored as the equations write them, [d_out, d_in] row-major,
+ * in the element type dtype; h is [T, d_model] in dtype.  Products
+ * accumulate in fp32.  d_model and d_cq are multiples of 32 (d_cq <= 2048).
+ * Each call takes a caller-owned device workspace of at least the size the
+ * matching *_workspace function returns (-1 there: invalid sizes); a smaller
+ * one is MLA_ERR_SHAPE.  The library allocates nothing.
+ */
+
+/* Workspace bytes of mla_kv_produce for T tokens of width d_model. */
+int64_t mla_kv_produce_workspace(int32_t T, int32_t d_model);
+
+/*
+ * mla_kv_produce - cache rows of T new tokens, written like mla_kv_append:
+ *   c^KV = RMSNorm(W^DKV h) (gain kv_gain [512], eps),  k^R = W^KR h,
+ *   cache[slot(seq_idx[r], pos[r])] = [ c^KV_r ; R_{pos[r]} k^R_r ]
+ * w_dkv [512, d_model], w_kr [64, d_model]; cache, block_table, seq_idx, pos,
+ * rope_base and the skipping of out-of-range rows as in mla_kv_append.
+ */
+int32_t mla_kv_produce(const void* h, const void* w_dkv, const float* kv_gain, const void* w_kr,
+                       int32_t T, int32_t d_model, int32_t dtype, float eps, float rope_base,
+                       void* kv_cache, int32_t num_blocks, int32_t block_size,
+                       const int32_t* block_table, int32_t num_seqs, int32_t max_blocks,
+                       const int32_t* seq_idx, const int32_t* pos, void* workspace,
+                       int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes of mla_q_produce. */
+int64_t mla_q_produce_workspace(int32_t T, int32_t d_model, int32_t d_cq, int32_t dtype);
+
+/*
+ * mla_q_produce - per-head queries of T tokens through the compressed query:
+ *   c^Q = RMSNorm(W^DQ h) (gain q_gain [d_cq], eps),
+ *   q_nope = W^UQ c^Q  -> [T, n_h, 128],  q_rope = W^QR c^Q -> [T, n_h, 64]
+ * (q_rope before rotation: mla_absorb_q rotates it).  w_dq [d_cq, d_model],
+ * w_uq [n_h * 128, d_cq], w_qr [n_h * 64, d_cq], head i owning rows i*128..
+ * and i*64..; c^Q is rounded to dtype before its up-projections.
+ */
+int32_t mla_q_produce(const void* h, const void* w_dq, const float* q_gain, const void* w_uq,
+                      const void* w_qr, int32_t T, int32_t d_model, int32_t d_cq, int32_t n_h,
+                      int32_t dtype, float eps, void* q_nope, void* q_rope, void* workspace,
+                      int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,8 @@ D_C, D_R, D_H, ROW, BLOCK = 512, 64, 128, 576, 64
 _EXPORTS = ("mla_status_string", "mla_abi_version", "mla_kv_append", "mla_absorb_q",
             "mla_decode_paged", "mla_splitkv_combine", "mla_out_proj", "mla_split_plan",
             "mla_plan_decode", "mla_decode_paged_planned", "mla_combine_planned",
-            "mla_out_proj_planned")
+            "mla_out_proj_planned", "mla_kv_produce_workspace", "mla_kv_produce",
+            "mla_q_produce_workspace", "mla_q_produce")
 
 
 class MLAError(RuntimeError):
@@ -65,6 +66,12 @@ def load() -> ctypes.CDLL:
                                           _P, _I, _P, _P, _P, _P, _P]),
         "mla_combine_planned": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
         "mla_out_proj_planned": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
+        "mla_kv_produce_workspace": (ctypes.c_int64, [_I, _I]),
+        "mla_kv_produce": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _F, _P, _I, _I, _P, _I, _I, _P,
+                                _P, _P, ctypes.c_int64, _P]),
+        "mla_q_produce_workspace": (ctypes.c_int64, [_I, _I, _I, _I]),
+        "mla_q_produce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P,
+                               ctypes.c_int64, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -342,3 +349,70 @@ def mla_out_proj_planned(o_lat, o_part, lse_part, split, w_uv, out, lse=None, st
         _dev(split, "split", torch.int32) if n_split else None, n_split, _dev(w_uv, "w_uv"), T,
         n_h, dt, _dev(out, "out", f32), _dev(lse, "lse", f32), _stream(stream))
     _check("mla_out_proj_planned", st)
+
+
+def mla_kv_produce_workspace(T, d_model):
+    """Workspace bytes of mla_kv_produce (see mla.h)."""
+    n = int(load().mla_kv_produce_workspace(int(T), int(d_model)))
+    if n < 0:
+        raise ValueError("invalid producer sizes")
+    return n
+
+
+def mla_kv_produce(h, w_dkv, kv_gain, w_kr, kv_cache, block_table, seq_idx, pos, rope_base,
+                   eps, workspace, stream=None):
+    """Cache rows of new tokens from their hidden states (see mla.h)."""
+    torch = _torch()
+    dt = _dtype_code(h)
+    T, d_model = int(h.shape[0]), int(h.shape[1])
+    if tuple(w_dkv.shape) != (D_C, d_model) or tuple(w_kr.shape) != (D_R, d_model):
+        raise ValueError("w_dkv must be [512, d_model] and w_kr [64, d_model]")
+    if tuple(kv_gain.shape) != (D_C,):
+        raise ValueError("kv_gain must be [512]")
+    if w_dkv.dtype != h.dtype or w_kr.dtype != h.dtype or kv_cache.dtype != h.dtype:
+        raise TypeError("h, the weights and the cache must share one dtype")
+    if workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    st = load().mla_kv_produce(
+        _dev(h, "h"), _dev(w_dkv, "w_dkv"), _dev(kv_gain, "kv_gain", torch.float32),
+        _dev(w_kr, "w_kr"), T, d_model, dt, float(eps), float(rope_base), _dev(kv_cache, "kv_cache"),
+        int(kv_cache.shape[0]), int(kv_cache.shape[1]), _dev(block_table, "block_table", torch.int32),
+        int(block_table.shape[0]), int(block_table.shape[1]), _dev(seq_idx, "seq_idx", torch.int32),
+        _dev(pos, "pos", torch.int32), _dev(workspace, "workspace"), int(workspace.numel()),
+        _stream(stream))
+    _check("mla_kv_produce", st)
+
+
+def mla_q_produce_workspace(T, d_model, d_cq, dtype_code):
+    """Workspace bytes of mla_q_produce (see mla.h)."""
+    n = int(load().mla_q_produce_workspace(int(T), int(d_model), int(d_cq), int(dtype_code)))
+    if n < 0:
+        raise ValueError("invalid producer sizes")
+    return n
+
+
+def mla_q_produce(h, w_dq, q_gain, w_uq, w_qr, q_nope, q_rope, eps, workspace, stream=None):
+    """Per-head queries of tokens through the compressed query (see mla.h)."""
+    torch = _torch()
+    dt = _dtype_code(h)
+    T, d_model = int(h.shape[0]), int(h.shape[1])
+    d_cq = int(w_dq.shape[0])
+    n_h = int(q_nope.shape[1])
+    if tuple(w_dq.shape) != (d_cq, d_model) or tuple(q_gain.shape) != (d_cq,):
+        raise ValueError("w_dq must be [d_cq, d_model] and q_gain [d_cq]")
+    if tuple(w_uq.shape) != (n_h * D_H, d_cq) or tuple(w_qr.shape) != (n_h * D_R, d_cq):
+        raise ValueError("w_uq must be [n_h*128, d_cq] and w_qr [n_h*64, d_cq]")
+    if tuple(q_nope.shape) != (T, n_h, D_H) or tuple(q_rope.shape) != (T, n_h, D_R):
+        raise ValueError("q_nope must be [T, n_h, 128] and q_rope [T, n_h, 64]")
+    for name, t in (("w_dq", w_dq), ("w_uq", w_uq), ("w_qr", w_qr), ("q_nope", q_nope),
+                    ("q_rope", q_rope)):
+        if t.dtype != h.dtype:
+            raise TypeError(f"{name} must have h's dtype")
+    if workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    st = load().mla_q_produce(
+        _dev(h, "h"), _dev(w_dq, "w_dq"), _dev(q_gain, "q_gain", torch.float32), _dev(w_uq, "w_uq"),
+        _dev(w_qr, "w_qr"), T, d_model, d_cq, n_h, dt, float(eps), _dev(q_nope, "q_nope"),
+        _dev(q_rope, "q_rope"), _dev(workspace, "workspace"), int(workspace.numel()),
+        _stream(stream))
+    _check("mla_q_produce", st)

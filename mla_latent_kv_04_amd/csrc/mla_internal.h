@@ -49,4 +49,18 @@ hipError_t launch_out_proj_planned(float* o_lat, const float* o_part, const floa
                                    const int* split, int n_split, const void* w_uv, int T, int n_h,
                                    int dtype, float* out, float* lse, hipStream_t stream);
 
+// Producers (produce.hip).  Workspace bytes as returned by the *_workspace
+// functions, 256-byte aligned.
+long kv_produce_workspace(int T, int d_model);
+long q_produce_workspace(int T, int d_model, int d_cq, int dtype);
+hipError_t launch_kv_produce(const void* h, const void* w_dkv, const float* kv_gain,
+                             const void* w_kr, int T, int d_model, int dtype, float eps,
+                             float base, void* cache, int num_blocks, const int* table,
+                             int num_seqs, int max_blocks, const int* seq_idx, const int* pos,
+                             void* workspace, hipStream_t stream);
+hipError_t launch_q_produce(const void* h, const void* w_dq, const float* q_gain,
+                            const void* w_uq, const void* w_qr, int T, int d_model, int d_cq,
+                            int n_h, int dtype, float eps, void* q_nope, void* q_rope,
+                            void* workspace, hipStream_t stream);
+
 }  // namespace mla

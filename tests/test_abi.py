@@ -22,7 +22,8 @@ def lib():
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int32_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int32_t|int64_t|const char\*)\s+(mla_\w+)\s*\(", text,
+                                 re.M)))
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -111,3 +112,42 @@ def test_split_plan_matches_oracle_rule():
 def test_split_plan_rejects_negative_length():
     with pytest.raises(B.MLAError):
         pkg.mla_split_plan(np.array([5, -1], dtype=np.int32), 2)
+
+
+def test_producers_reject_bad_arguments_and_size_their_workspace(lib):
+    ws = lib.mla_kv_produce_workspace
+    assert ws(128, 5120) > 0 and ws(0, 5120) == 0
+    assert ws(128, 5121) == -1 and ws(-1, 5120) == -1 and ws(128, 16) == -1
+    assert ws(256, 5120) >= ws(128, 5120)
+    need = ws(4, 64)
+
+    def kv(**kw):
+        a = dict(h=FAKE, wd=FAKE, g=FAKE, wk=FAKE, T=4, dm=64, dt=1, eps=1e-6, base=1e4, kv=FAKE,
+                 nb=4, bs=64, tab=FAKE, ns=1, mb=4, seq=FAKE, pos=FAKE, w=FAKE, wb=need)
+        a.update(kw)
+        return lib.mla_kv_produce(a["h"], a["wd"], a["g"], a["wk"], a["T"], a["dm"], a["dt"],
+                                  a["eps"], a["base"], a["kv"], a["nb"], a["bs"], a["tab"],
+                                  a["ns"], a["mb"], a["seq"], a["pos"], a["w"], a["wb"], None)
+    assert kv(dt=3) == 4
+    assert kv(dm=48) == 2 and kv(bs=32) == 2 and kv(eps=-1.0) == 2 and kv(base=0.0) == 2
+    assert kv(wb=need - 1) == 2                      # workspace too small
+    assert kv(h=NULL) == 1 and kv(w=NULL) == 1
+    assert kv(kv=MISALIGNED) == 3
+    assert kv(T=0, h=NULL, w=NULL) == 0              # nothing to do
+    qws = lib.mla_q_produce_workspace
+    assert qws(128, 5120, 1536, 1) > 0 and qws(128, 5120, 4096, 1) == -1
+    assert qws(128, 5120, 1536, 7) == -1
+    qneed = qws(4, 64, 64, 1)
+
+    def q(**kw):
+        a = dict(h=FAKE, wd=FAKE, g=FAKE, wu=FAKE, wr=FAKE, T=4, dm=64, dq=64, nh=2, dt=1,
+                 eps=1e-6, qn=FAKE, qr=FAKE, w=FAKE, wb=qneed)
+        a.update(kw)
+        return lib.mla_q_produce(a["h"], a["wd"], a["g"], a["wu"], a["wr"], a["T"], a["dm"],
+                                 a["dq"], a["nh"], a["dt"], a["eps"], a["qn"], a["qr"], a["w"],
+                                 a["wb"], None)
+    assert q(dt=5) == 4
+    assert q(dq=40) == 2 and q(dq=4096) == 2 and q(nh=0) == 2 and q(wb=qneed - 1) == 2
+    assert q(wu=NULL) == 1
+    assert q(wd=MISALIGNED) == 3
+    assert q(T=0, h=NULL) == 0
