@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 MFMA_F32_PEAK_TFLOPS = 157.3
+PRODUCER_EPS = 1e-6           # RMSNorm epsilon of the latent and query norms
 
 # sources of the attention kernels; the committed HBM-traffic record is only
 # used while these are unchanged
@@ -82,9 +83,24 @@ def load_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(prob, budget_s: float):
+def producer_work(T, n_h, d_model, d_cq, esz):
+    """(kv bytes, q bytes, kv flops, q flops) of the two producers for T tokens.
+
+    Bytes: the hidden states and every weight read once, the gains, and the
+    outputs written once (cache rows of 576; q^C and q^R of n_h * 192 per
+    token); c^Q's round trip through the workspace is not counted.  FLOPs:
+    2 per multiply-add of the projections."""
+    kv_w = (512 + 64) * d_model
+    q_w = d_cq * d_model + n_h * (128 + 64) * d_cq
+    kv_by = (T * d_model + kv_w + T * 576) * esz + 512 * 4
+    q_by = (T * d_model + q_w + T * n_h * 192) * esz + d_cq * 4
+    return kv_by, q_by, 2 * T * kv_w, 2 * T * q_w
+
+
+def cpu_baseline(prob, budget_s: float, hid=None):
     """Time the float64 oracle on whole sequences (all heads) until the budget
-    is spent; returns tokens/s over the sample."""
+    is spent; returns tokens/s over the sample.  With hidden states, each
+    sequence's new row and queries come from the oracle's producers first."""
     import numpy as np
     from oracle import mla_oracle as orc
     from mla_latent_kv_04_amd.workloads import ROPE_BASE, softmax_scale
@@ -105,7 +121,16 @@ def cpu_baseline(prob, budget_s: float):
         L = int(prob.seq_lens[b])
         vis = orc.visible_keys(L, q)
         sl = slice(b * q, b * q + rows_per_call)
-        orc.mla_attention_naive(c[:L], k[:L], prob.q_nope[sl], prob.q_rope[sl], prob.w_uk,
+        q_nope, q_rope = prob.q_nope[sl], prob.q_rope[sl]
+        if hid is not None:
+            # the step's rows are the last q of the sequence, its tokens b q ..
+            c, k = c.copy(), k.copy()
+            c[L - q:], k[L - q:], _ = orc.kv_produce(hid.h[b * q:(b + 1) * q], hid.w_dkv,
+                                                     hid.kv_gain, hid.w_kr,
+                                                     np.arange(L - q, L), ROPE_BASE, PRODUCER_EPS)
+            _, q_nope, q_rope = orc.q_produce(hid.h[sl], hid.w_dq, hid.q_gain, hid.w_uq,
+                                              hid.w_qr, wl.n_h, PRODUCER_EPS)
+        orc.mla_attention_naive(c[:L], k[:L], q_nope, q_rope, prob.w_uk,
                                 prob.w_uv, np.arange(L), prob.q_pos[sl], vis[:rows_per_call],
                                 softmax_scale(), ROPE_BASE)
         done_rows += rows_per_call
@@ -132,6 +157,9 @@ def main():
                     help="split-KV partitions per row; 0 = balanced work plan (default: workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--from-hidden", action="store_true",
+                    help="start the step from hidden states: the cache-row and query producers "
+                         "(DeepSeek-V2 widths) replace the append and the given queries")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run one plain device-to-device copy of this many bytes (a "
                          "known-size reference for hardware byte counters)")
@@ -146,9 +174,14 @@ def main():
     import torch
     from mla_latent_kv_04_amd import _binding as mla
     from mla_latent_kv_04_amd import pipeline
-    from mla_latent_kv_04_amd.workloads import ROPE_BASE, WORKLOADS, make_problem, softmax_scale
+    from mla_latent_kv_04_amd.workloads import (D_CQ_V2, D_MODEL_V2, ROPE_BASE, WORKLOADS,
+                                                make_hidden, make_problem, softmax_scale)
 
     wl = WORKLOADS[args.workload]
+    if args.from_hidden and wl.n_h != 128:
+        print("--from-hidden uses the DeepSeek-V2 widths (128 heads, query compression); "
+              f"{wl.name} has {wl.n_h} heads", file=sys.stderr)
+        sys.exit(2)
     splits = args.splits if args.splits is not None else wl.num_splits
     log(f"[bench] generating {wl.name} (splits={splits})")
     prob = make_problem(wl)
@@ -157,10 +190,36 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     scale = softmax_scale()
+    hid = hw = None
+    if args.from_hidden:
+        log("[bench] generating hidden states and producer weights")
+        hid = make_hidden(prob)
+        hw = {k: (torch.from_numpy(v).cuda() if k.endswith("gain")
+                  else pipeline._to_device(v, dp.dtype, "cuda"))
+              for k, v in vars(hid).items()}
+        code = 1 if wl.dtype == "bf16" else 0
+        hw["ws_kv"] = torch.empty(mla.mla_kv_produce_workspace(prob.T, D_MODEL_V2),
+                                  dtype=torch.uint8, device="cuda")
+        hw["ws_q"] = torch.empty(mla.mla_q_produce_workspace(prob.T, D_MODEL_V2, D_CQ_V2, code),
+                                 dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
 
     def one_step(ev=None):
-        mla.mla_kv_append(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r, dp.new_seq,
-                          dp.new_pos, ROPE_BASE)
+        if hw is None:
+            mla.mla_kv_append(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r, dp.new_seq,
+                              dp.new_pos, ROPE_BASE)
+        else:
+            if ev is not None:
+                ev[2].record(stream)
+            mla.mla_kv_produce(hw["h"], hw["w_dkv"], hw["kv_gain"], hw["w_kr"], dp.kv_cache,
+                               dp.block_table, dp.new_seq, dp.new_pos, ROPE_BASE, PRODUCER_EPS,
+                               hw["ws_kv"])
+            if ev is not None:
+                ev[3].record(stream)
+            mla.mla_q_produce(hw["h"], hw["w_dq"], hw["q_gain"], hw["w_uq"], hw["w_qr"],
+                              dp.q_nope, dp.q_rope, PRODUCER_EPS, hw["ws_q"])
+            if ev is not None:
+                ev[4].record(stream)
         mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE)
         if ev is not None:
             ev[0].record(stream)
@@ -200,7 +259,8 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    n_ev = 5 if hw is not None else 2
+    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(n_ev))
               for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -210,7 +270,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     tokens = prob.T
     value = tokens / (ms_per_step * 1e-3)
 
@@ -229,17 +289,36 @@ def main():
     log(f"[bench] step {ms_per_step:.4f} ms, attention kernel {dec_ms * 1e3:.1f} us, "
         f"{gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
 
+    producers = None
+    if hw is not None:
+        kv_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+        q_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
+        kv_by, q_by, kv_fl, q_fl = producer_work(prob.T, wl.n_h, D_MODEL_V2, D_CQ_V2,
+                                                 2 if wl.dtype == "bf16" else 4)
+        producers = {
+            "d_model": D_MODEL_V2, "d_cq": D_CQ_V2,
+            "kv_us": round(kv_ms * 1e3, 2), "q_us": round(q_ms * 1e3, 2),
+            "kv_algorithmic_bytes": kv_by, "q_algorithmic_bytes": q_by,
+            "kv_hbm_frac": round(kv_by / (kv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "q_hbm_frac": round(q_by / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kv_mfma_frac": round(kv_fl / (kv_ms * 1e-3) / 1e12 / mfma_peak, 4),
+            "q_mfma_frac": round(q_fl / (q_ms * 1e-3) / 1e12 / mfma_peak, 4),
+        }
+        log(f"[bench] producers: kv {kv_ms * 1e3:.1f} us, q {q_ms * 1e3:.1f} us")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_seconds} s)")
-        cpu = cpu_baseline(prob, args.cpu_seconds)
+        cpu = cpu_baseline(prob, args.cpu_seconds, hid)
 
     cfg = {"workload": wl.name, "B": wl.B, "n_h": wl.n_h, "q_len": wl.q_len,
            "context": (f"U[{wl.ctx[0]},{wl.ctx[1]}]" if isinstance(wl.ctx, tuple) else wl.ctx),
            "block_size": wl.block_size,
            "split_kv": ("balanced plan" if splits == 0 else f"{splits} per row"),
            "work_items": (int(dp.work.shape[0]) if splits == 0 else dp.B * dp.q_len * splits),
-           "d_c": 512, "d_R": 64, "d_h": 128}
+           "d_c": 512, "d_R": 64, "d_h": 128,
+           "step_input": ("hidden states (cache-row and query producers in the step)"
+                          if hw is not None else "new latent rows and per-head queries")}
     rec = {
         "metric": "MLA decode tokens/s (+ attention-kernel HBM GB/s and MFMA share of peak), "
                   "DeepSeek-V2 head shape",
@@ -255,6 +334,8 @@ def main():
                              "source_sha": source_sha()},
         "cpu_baseline": cpu,
     }
+    if producers is not None:
+        rec["producers"] = producers
     print(json.dumps(rec), flush=True)
 
 

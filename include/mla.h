@@ -293,7 +293,10 @@ int32_t mla_out_proj_planned(float* o_lat, const float* o_part, const float* lse
  *   RMSNorm(x) = g * x / sqrt(mean(x^2) + eps), g a learned gain (fp32).
  * Weights are stored as the equations write them, [d_out, d_in] row-major,
  * in the element type dtype; h is [T, d_model] in dtype.  Products
- * accumulate in fp32.  d_model and d_cq are multiples of 32 (d_cq <= 2048).
+ * accumulate in fp32.  d_model and d_cq are multiples of 64 (d_cq <= 2048),
+ * and every operand's element count (T * d_model, T * d_cq, n_h * 128 * d_cq)
+ * stays below 2^29 (else MLA_ERR_SHAPE).  q_nope and q_rope are 16-byte
+ * aligned.
  * Each call takes a caller-owned device workspace of at least the size the
  * matching *_workspace function returns (-1 there: invalid sizes); a smaller
  * one is MLA_ERR_SHAPE.  The library allocates nothing.

@@ -8,15 +8,16 @@
 //                                                   the latent RMSNorm of its §3.1.1)
 //
 // Every projection is Y = X W^T with both operands' reduced axis contiguous
-// (X [T, K] rows, W [N, K] rows as eq. 9 writes them), so MFMA fragments load
-// straight from memory.  A workgroup of four waves computes 64 outputs for
-// 128 rows over one slice of K: wave w owns outputs 16w..16w+15 (A = W rows)
-// and all 128 rows (B = X rows, shared by the four waves through L1).  For the
-// decode sizes the weights dominate the bytes and are read once; the narrow
-// projections (576 and 1536 outputs) split K over workgroups to fill the chip,
-// writing fp32 partial sums that the epilogue kernels add up before the
-// RMSNorm, the key rotation and the paged write.  No LDS: occupancy hides the
-// load latency.
+// (X [T, K] rows, W [N, K] rows as eq. 9 writes them).  For decode sizes the
+// weights dominate the bytes and are read once.  In bf16 a workgroup computes
+// a tile of 128 W rows x 128 (or 64) X rows with four waves of MFMA tiles;
+// K advances in stages of 64 that direct global->LDS loads bring in, four
+// (three) stages resident and three (two) in flight, and the two projections
+// that share an input (W^DKV and W^KR; W^UQ and W^QR) run in one launch.
+// Narrow projections (576 or d_cq outputs) split K over workgroups to fill
+// the chip and write fp32 partial sums; one workgroup per token adds them up
+// before the RMSNorm (and, for the cache row, the key rotation and the paged
+// write).  fp32 takes a plain MFMA kernel without LDS.
 #include <algorithm>
 
 #include "mla_common.h"
@@ -26,13 +27,13 @@ namespace mla {
 
 namespace {
 
-constexpr int GN = 64;    // outputs per workgroup
-constexpr int GT = 128;   // rows per workgroup
+constexpr int GN = 64;    // fp32: outputs per workgroup
+constexpr int GT = 128;   // fp32: rows per workgroup
 
-// Y[z] = X[:, kz] W[:, kz]^T over K slice z (kz = [z kc, min(K, (z+1) kc))),
+// fp32: Y[z] = X[:, kz] W[:, kz]^T over K slice z (kz = [z kc, min(K, (z+1) kc))),
 // written to columns col0 .. col0 + N - 1 of rows of ldo elements.  DIRECT:
-// one slice, converted to the element type into out [T, ldo]; else fp32
-// partials into part [S, T, ldo].
+// one slice, into out [T, ldo]; else partials into part [S, T, ldo].  Wave w
+// owns outputs 16w..16w+15 (A = W rows) and all 128 rows (B = X rows).
 template <class E, bool DIRECT>
 __global__ void __launch_bounds__(256) gemm_nt_kernel(const typename E::storage* __restrict__ X,
                                                       const typename E::storage* __restrict__ W,
@@ -85,6 +86,175 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(const typename E::storage*
   }
 }
 
+// bf16 tiles ----------------------------------------------------------------
+constexpr int PN = 128;                        // W rows (outputs) per workgroup
+constexpr int PK = 64;                         // K slices are multiples of this
+
+// One direct global->LDS load: lane l's 16 bytes at base + lane_off land at
+// LDS byte lds_dst + 16 l (M0 holds the LDS address; one wait state before
+// the load reads it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is named as clobbered on purpose
+__device__ __forceinline__ void dma16(unsigned lds_dst, const char* base, unsigned lane_off) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %2"
+      :
+      : "v"(lane_off), "s"(lds_dst), "s"(base)
+      : "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most VMC of this wave's vector-memory loads are in flight
+// and its LDS reads are done, then a workgroup barrier.
+template <int VMC>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(VMC >= 0 && VMC < 64, "vmcnt field");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((VMC & 15) | ((VMC >> 4) << 14) | 0x70);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One projection of a bf16 launch: W [N, K]; DIRECT: bf16 out rows of ldo
+// elements, columns col0..; else fp32 partials part [S, T, ldo].
+struct ProjOut {
+  const uint16_t* W;
+  int N;
+  void* out;
+  int ldo;
+  int col0;
+};
+
+// Workgroup (x, y, z): W rows n0 .. n0 + 127 of projection p0 (x < tiles0)
+// or p1, X rows TT y .. TT y + TT - 1, K slice [z kc, min(K, (z + 1) kc)),
+// kc a multiple of KS.  Four waves in a 2 x 2 grid: wave (wn, wt) computes
+// W rows 64 wn.. against X rows TT/2 wt.. with 4 x TT/32 MFMA tiles.
+//
+// A stage holds KS of K: 128 + TT rows of 2 KS bytes (the W rows, then the
+// X rows); 16-byte piece q of stage row R sits in slot q ^ (R & 7), so that
+// the eight lanes of one ds_read_b128 phase (eight rows, one piece) hit
+// eight different bank groups.  Direct load i of a stage fills the 1024
+// bytes of rows RPI i .. RPI i + RPI - 1; wave w issues loads
+// w NIW .. w NIW + NIW - 1.  Rows past N or T re-read the last valid row;
+// their results are dropped.  NST stages are resident, NST - 1 in flight.
+template <bool DIRECT, int TT, int NST, int KS>
+__global__ void __launch_bounds__(256, (NST * (PN + TT) * KS * 2) <= 80 * 1024 ? 2 : 1)
+    proj_bf16_kernel(const uint16_t* __restrict__ X, int T, int K, int kc, ProjOut p0,
+                     ProjOut p1, int tiles0) {
+  constexpr int P_ROWB = KS * 2;               // bytes of one row in a stage
+  constexpr int SPR = P_ROWB / 16;             // 16-byte slots per row
+  constexpr int RPI = 64 / SPR;                // rows per direct load
+  constexpr int STAGE = (PN + TT) * P_ROWB;
+  constexpr int NIW = STAGE / 1024 / 4;
+  constexpr int TB = TT / 32;                  // MFMA row tiles of X per wave
+  static_assert(KS == 64 || KS == 128, "stage K");
+  __shared__ __attribute__((aligned(16))) char smem[NST * STAGE];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const bool second = (int)blockIdx.x >= tiles0;
+  const ProjOut p = second ? p1 : p0;
+  const int n0 = ((int)blockIdx.x - (second ? tiles0 : 0)) * PN;
+  const int t0 = blockIdx.y * TT;
+  const int k0 = blockIdx.z * kc;
+  const int nst = (min(K, k0 + kc) - k0) / KS;
+
+  unsigned off[NIW];
+#pragma unroll
+  for (int j = 0; j < NIW; ++j) {
+    const int R = RPI * (wave * NIW + j) + lane / SPR;   // stage row
+    const int row = R < PN ? min(n0 + R, p.N - 1) : min(t0 + R - PN, T - 1);
+    off[j] = (unsigned)row * (unsigned)(K * 2) + (unsigned)(((lane % SPR) ^ (R & 7)) * 16);
+  }
+  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  auto issue = [&](int s) __attribute__((always_inline)) {
+    const long kb = (long)(k0 + s * KS) * 2;
+    const char* wb = reinterpret_cast<const char*>(p.W) + kb;
+    const char* xb = reinterpret_cast<const char*>(X) + kb;
+    const unsigned dst = lds0 + (unsigned)((s % NST) * STAGE + wave * NIW * 1024);
+#pragma unroll
+    for (int j = 0; j < NIW; ++j)
+      dma16(dst + j * 1024, RPI * (wave * NIW + j) < PN ? wb : xb, off[j]);
+  };
+
+  // lane (g, r16) of MFMA tile (i, j) reads piece 4 ks + g of W row
+  // 64 wn + 16 i + r16 and of X row TT/2 wt + 16 j + r16
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wn = wave & 1, wt = wave >> 1;
+  const int a_off = (64 * wn + r16) * P_ROWB, b_off = (PN + (TT / 2) * wt + r16) * P_ROWB;
+  f32x4_t acc[4][TB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TB; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
+  auto compute = [&](int s) __attribute__((always_inline)) {
+    const char* st = smem + (s % NST) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < KS / 32; ++ks) {
+      const int sw = ((4 * ks + g) ^ (r16 & 7)) * 16;
+      i16x8_t a[4], b[TB];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const i16x8_t*>(st + a_off + 16 * i * P_ROWB + sw);
+#pragma unroll
+      for (int j = 0; j < TB; ++j)
+        b[j] = *reinterpret_cast<const i16x8_t*>(st + b_off + 16 * j * P_ROWB + sw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16((bf16x8_t)a[i], (bf16x8_t)b[j],
+                                                              acc[i][j], 0, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nst) issue(s);
+  for (int s = 0; s < nst; ++s) {
+    // stage s landed: stages s + 1 .. min(s + NST - 2, nst - 1) stay in flight
+    const int ahead = min(NST - 2, nst - 1 - s);
+    if constexpr (NST == 4) {
+      if (ahead == 2)
+        stage_barrier<2 * NIW>();
+      else if (ahead == 1)
+        stage_barrier<NIW>();
+      else
+        stage_barrier<0>();
+    } else {
+      static_assert(NST == 3, "three or four stages");
+      if (ahead == 1)
+        stage_barrier<NIW>();
+      else
+        stage_barrier<0>();
+    }
+    if (s + NST - 1 < nst) issue(s + NST - 1);   // into the slot every wave finished with
+    compute(s);
+  }
+
+  // acc[i][j][e]: output n0 + 64 wn + 16 i + 4 g + e of row t0 + TT/2 wt + 16 j + r16
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    const int t = t0 + (TT / 2) * wt + 16 * j + r16;
+    if (t >= T) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 64 * wn + 16 * i + 4 * g;
+      if (n >= p.N) continue;
+      if constexpr (DIRECT) {
+        uint16_t* o = static_cast<uint16_t*>(p.out) + (long)t * p.ldo + p.col0 + n;
+        *reinterpret_cast<uint2*>(o) = uint2{pack_bf16x2(acc[i][j][0], acc[i][j][1]),
+                                             pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+      } else {
+        float* o = static_cast<float*>(p.out) + ((long)blockIdx.z * T + t) * p.ldo + p.col0 + n;
+        *reinterpret_cast<float4*>(o) = float4{acc[i][j][0], acc[i][j][1], acc[i][j][2],
+                                               acc[i][j][3]};
+      }
+    }
+  }
+}
+
 // Sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -92,10 +262,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One wave per new token: add the S partial rows [576], RMSNorm the 512
-// latent features (gain, eps), rotate the 32 key pairs at the token's
-// position and write the row into its cache slot (the slot rule and the
-// skipping of out-of-range rows are those of the append).
+// One workgroup per new token: wave w adds partial rows w, w + 4, .. of the
+// S partial rows [576] (four at a time, all loads in flight; a row past S is
+// re-read with weight 0); wave 0 adds the four sums, RMSNorms the 512 latent
+// features (gain, eps), rotates the 32 key pairs at the token's position and
+// writes the row into its cache slot (the slot rule and the skipping of
+// out-of-range rows are those of the append).
 template <class E>
 __global__ void __launch_bounds__(256) kv_epilogue_kernel(
     const float* __restrict__ part, int S, int T, const float* __restrict__ gain, float eps,
@@ -103,30 +275,57 @@ __global__ void __launch_bounds__(256) kv_epilogue_kernel(
     int num_seqs, int max_blocks, const int* __restrict__ seq_idx, const int* __restrict__ pos,
     double base) {
   using Ts = typename E::storage;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = lane_id();
-  if (r >= T) return;
+  __shared__ float red[4][ROW];
+  const int r = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
   const int b = seq_idx[r];
   const int p = pos[r];
   if (b < 0 || b >= num_seqs || p < 0 || p / BLOCK >= max_blocks) return;
   const int blk = table[(long)b * max_blocks + p / BLOCK];
   if (blk < 0 || blk >= num_blocks) return;
-  Ts* dst = cache + ((long)blk * BLOCK + (p % BLOCK)) * ROW;
-  // latent features 8 lane .. 8 lane + 7
+  // latent features 8 lane .. 8 lane + 7; key pair lane & 31 (kept by lanes < 32)
   float y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float kx = 0.0f, ky = 0.0f;
-  for (int z = 0; z < S; ++z) {
-    const float* row = part + ((long)z * T + r) * ROW;
-    const float4 u = reinterpret_cast<const float4*>(row + 8 * lane)[0];
-    const float4 v = reinterpret_cast<const float4*>(row + 8 * lane)[1];
-    y[0] += u.x; y[1] += u.y; y[2] += u.z; y[3] += u.w;
-    y[4] += v.x; y[5] += v.y; y[6] += v.z; y[7] += v.w;
-    if (lane < D_R / 2) {
-      const float2 w = reinterpret_cast<const float2*>(row + D_C)[lane];
-      kx += w.x;
-      ky += w.y;
+  for (int z0 = wave; z0 < S; z0 += 16) {
+    float4 u[4], v[4];
+    float2 w[4];
+    float m[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int z = z0 + 4 * q;
+      m[q] = z < S ? 1.0f : 0.0f;
+      const float* row = part + ((long)min(z, S - 1) * T + r) * ROW;
+      u[q] = reinterpret_cast<const float4*>(row + 8 * lane)[0];
+      v[q] = reinterpret_cast<const float4*>(row + 8 * lane)[1];
+      w[q] = reinterpret_cast<const float2*>(row + D_C)[lane & 31];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      y[0] += m[q] * u[q].x; y[1] += m[q] * u[q].y; y[2] += m[q] * u[q].z; y[3] += m[q] * u[q].w;
+      y[4] += m[q] * v[q].x; y[5] += m[q] * v[q].y; y[6] += m[q] * v[q].z; y[7] += m[q] * v[q].w;
+      kx += m[q] * w[q].x;
+      ky += m[q] * w[q].y;
     }
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[wave][8 * lane + j] = y[j];
+  if (lane < D_R / 2) {
+    red[wave][D_C + 2 * lane] = kx;
+    red[wave][D_C + 2 * lane + 1] = ky;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = 8 * lane + j;
+    y[j] = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+  }
+  if (lane < D_R / 2) {
+    const int c = D_C + 2 * lane;
+    kx = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+    ky = (red[0][c + 1] + red[1][c + 1]) + (red[2][c + 1] + red[3][c + 1]);
+  }
+  Ts* dst = cache + ((long)blk * BLOCK + (p % BLOCK)) * ROW;
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) ss += y[j] * y[j];
@@ -150,61 +349,127 @@ __global__ void __launch_bounds__(256) kv_epilogue_kernel(
   }
 }
 
-// One workgroup per token: add the S partial rows [d], RMSNorm them (gain,
-// eps) and store the compressed query c^Q [T, d] in the element type.
+// One workgroup per token: wave w adds partial rows w, w + 4, .. of the S
+// partial rows [d] (d <= 2048, a multiple of 64; four rows at a time, all
+// loads in flight, a row past S re-read with weight 0); then every thread
+// adds the four sums of its features, and the token's row is RMSNormed
+// (gain, eps) and stored as c^Q [T, d] in the element type.
 template <class E>
 __global__ void __launch_bounds__(256) q_norm_kernel(const float* __restrict__ part, int S, int T,
                                                      int d, const float* __restrict__ gain,
                                                      float eps,
                                                      typename E::storage* __restrict__ c_q) {
-  __shared__ float red[4];
+  __shared__ float red[4][2048];
+  __shared__ float ssum[4];
   const int t = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  // lane's float4 columns lane + 64 j (j < 8, below d / 4)
+  const int n4 = d / 4;
+  float4 y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = float4{0, 0, 0, 0};
+  for (int z0 = wave; z0 < S; z0 += 16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int z = z0 + 4 * q;
+      const float m = z < S ? 1.0f : 0.0f;
+      const float4* row = reinterpret_cast<const float4*>(part + ((long)min(z, S - 1) * T + t) * d);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (64 * j >= n4) break;
+        const float4 u = row[min(lane + 64 * j, n4 - 1)];
+        y[j].x += m * u.x; y[j].y += m * u.y; y[j].z += m * u.z; y[j].w += m * u.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (lane + 64 * j < n4) reinterpret_cast<float4*>(red[wave])[lane + 64 * j] = y[j];
+  __syncthreads();
+  float v[8];
   float ss = 0.0f;
-  // d <= 256 * 8: every thread holds up to 8 features
-  float y[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = threadIdx.x + 256 * j;
-    float v = 0.0f;
-    if (i < d)
-      for (int z = 0; z < S; ++z) v += part[((long)z * T + t) * d + i];
-    y[j] = v;
-    ss += v * v;
+    v[j] = i < d ? (red[0][i] + red[1][i]) + (red[2][i] + red[3][i]) : 0.0f;
+    ss += v[j] * v[j];
   }
   ss = wave_sum(ss);
-  if (lane_id() == 0) red[threadIdx.x >> 6] = ss;
+  if (lane == 0) ssum[wave] = ss;
   __syncthreads();
-  const float rs = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+  const float rs = 1.0f / sqrtf((ssum[0] + ssum[1] + ssum[2] + ssum[3]) / (float)d + eps);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = threadIdx.x + 256 * j;
-    if (i < d) c_q[(long)t * d + i] = E::from_f32(y[j] * rs * gain[i]);
+    if (i < d) c_q[(long)t * d + i] = E::from_f32(v[j] * rs * gain[i]);
   }
 }
 
-// Slices of K per projection: enough workgroups to fill the chip (about 512),
-// each slice a multiple of 32 and at least 256 long.
-int k_slices(int T, int N, int K) {
-  const long tiles = (long)((N + GN - 1) / GN) * ((T + GT - 1) / GT);
-  if (tiles == 0 || tiles >= 256) return 1;
-  const int by_fill = (int)((512 + tiles - 1) / tiles);
-  return std::max(1, std::min(by_fill, K / 256));
+// Rows of X per bf16 workgroup: 128 (more reuse of each staged tile), or 64
+// for a projection so narrow that it splits K (twice the workgroups for the
+// same partial-sum bytes).  Measured on the decode shapes (T = 128): the
+// W^UQ + W^QR launch of 128 heads runs 8% faster with 128-row tiles, the
+// split W^DQ and W^DKV + W^KR ones 0-30% faster with 64.
+int t_tile(int T, int N) {
+  const long tiles128 = (long)((N + PN - 1) / PN) * ((T + 127) / 128);
+  return tiles128 < 128 ? 64 : 128;
 }
-int k_chunk(int K, int S) { return ((K + S - 1) / S + 31) / 32 * 32; }
 
-// One projection: W [N, K] against X [T, K] into columns col0.. of rows of
-// ldo; S K-slices of fp32 partials (S > 1 or !direct) or the element type.
+// K slice length of a projection with N outputs for T rows: enough
+// workgroups to fill the chip (about 256), each slice a multiple of 64 and
+// at least 512 long, so that the fp32 partials it writes stay well below the
+// weight bytes it reads.  The slice count is ceil(K / length).
+int k_chunk(int T, int N, int K) {
+  const int tt = t_tile(T, N);
+  const long tiles = (long)((N + PN - 1) / PN) * ((T + tt - 1) / tt);
+  int S = 1;
+  if (tiles > 0 && tiles < 128)
+    S = (int)std::max(1L, std::min((256 + tiles - 1) / tiles, (long)(K / 512)));
+  return ((K + S - 1) / S + PK - 1) / PK * PK;
+}
+int k_slices(int T, int N, int K) {
+  const int kc = k_chunk(T, N, K);
+  return (K + kc - 1) / kc;
+}
+
+// fp32: one projection W [N, K] against X [T, K] into columns col0.. of rows
+// of ldo, in K slices of kc (DIRECT: one slice, element-type output).
 template <class E>
-void gemm(const void* X, const void* W, int T, int N, int K, int S, bool direct, float* part,
-          int ldo, int col0, void* out, hipStream_t stream) {
+void gemm_f32(const void* X, const void* W, int T, int N, int K, int kc, bool direct,
+              float* part, int ldo, int col0, void* out, hipStream_t stream) {
   using Ts = typename E::storage;
+  const int S = (K + kc - 1) / kc;
   dim3 grid((N + GN - 1) / GN, (T + GT - 1) / GT, S), block(256);
   if (direct)
     hipLaunchKernelGGL((gemm_nt_kernel<E, true>), grid, block, 0, stream, (const Ts*)X,
-                       (const Ts*)W, T, N, K, k_chunk(K, S), nullptr, ldo, col0, (Ts*)out);
+                       (const Ts*)W, T, N, K, kc, nullptr, ldo, col0, (Ts*)out);
   else
     hipLaunchKernelGGL((gemm_nt_kernel<E, false>), grid, block, 0, stream, (const Ts*)X,
-                       (const Ts*)W, T, N, K, k_chunk(K, S), part, ldo, col0, nullptr);
+                       (const Ts*)W, T, N, K, kc, part, ldo, col0, nullptr);
+}
+
+// bf16: the projections p0 and p1 (p1.N == 0: none) of X [T, K], one launch.
+void proj_bf16(const void* X, int T, int K, int kc, bool direct, ProjOut p0, ProjOut p1,
+               hipStream_t stream) {
+  const int tiles0 = (p0.N + PN - 1) / PN, tiles1 = (p1.N + PN - 1) / PN;
+  const int tt = t_tile(T, p0.N + p1.N);
+  dim3 grid(tiles0 + tiles1, (T + tt - 1) / tt, (K + kc - 1) / kc), block(256);
+  const auto* x = static_cast<const uint16_t*>(X);
+  if (tt == 64) {
+    if (direct)
+      hipLaunchKernelGGL((proj_bf16_kernel<true, 64, 3, 64>), grid, block, 0, stream, x, T, K, kc, p0,
+                         p1, tiles0);
+    else
+      hipLaunchKernelGGL((proj_bf16_kernel<false, 64, 3, 64>), grid, block, 0, stream, x, T, K, kc,
+                         p0, p1, tiles0);
+  } else {
+    if (direct)
+      hipLaunchKernelGGL((proj_bf16_kernel<true, 128, 4, 64>), grid, block, 0, stream, x, T, K, kc,
+                         p0, p1, tiles0);
+    else
+      hipLaunchKernelGGL((proj_bf16_kernel<false, 128, 4, 64>), grid, block, 0, stream, x, T, K, kc,
+                         p0, p1, tiles0);
+  }
 }
 
 template <class E>
@@ -213,14 +478,21 @@ hipError_t kv_produce(const void* h, const void* w_dkv, const float* kv_gain, co
                       const int* table, int num_seqs, int max_blocks, const int* seq_idx,
                       const int* pos, void* workspace, hipStream_t stream) {
   float* part = static_cast<float*>(workspace);
-  const int S = k_slices(T, ROW, d_model);
+  const int kc = k_chunk(T, ROW, d_model);
+  const int S = (d_model + kc - 1) / kc;
   // the latent and the key projections fill columns 0..511 and 512..575 of
   // one partial buffer [S, T, 576]
-  gemm<E>(h, w_dkv, T, D_C, d_model, S, false, part, ROW, 0, nullptr, stream);
-  gemm<E>(h, w_kr, T, D_R, d_model, S, false, part, ROW, D_C, nullptr, stream);
-  hipLaunchKernelGGL(kv_epilogue_kernel<E>, dim3((T + 3) / 4), dim3(256), 0, stream, part, S, T,
-                     kv_gain, eps, (typename E::storage*)cache, num_blocks, table, num_seqs,
-                     max_blocks, seq_idx, pos, (double)base);
+  if constexpr (E::bytes == 2) {
+    proj_bf16(h, T, d_model, kc, false,
+              ProjOut{static_cast<const uint16_t*>(w_dkv), D_C, part, ROW, 0},
+              ProjOut{static_cast<const uint16_t*>(w_kr), D_R, part, ROW, D_C}, stream);
+  } else {
+    gemm_f32<E>(h, w_dkv, T, D_C, d_model, kc, false, part, ROW, 0, nullptr, stream);
+    gemm_f32<E>(h, w_kr, T, D_R, d_model, kc, false, part, ROW, D_C, nullptr, stream);
+  }
+  hipLaunchKernelGGL(kv_epilogue_kernel<E>, dim3(T), dim3(256), 0, stream, part, S, T, kv_gain,
+                     eps, (typename E::storage*)cache, num_blocks, table, num_seqs, max_blocks,
+                     seq_idx, pos, (double)base);
   return hipGetLastError();
 }
 
@@ -228,15 +500,28 @@ template <class E>
 hipError_t q_produce(const void* h, const void* w_dq, const float* q_gain, const void* w_uq,
                      const void* w_qr, int T, int d_model, int d_cq, int n_h, float eps,
                      void* q_nope, void* q_rope, void* workspace, hipStream_t stream) {
-  const int S = k_slices(T, d_cq, d_model);
+  const int kc = k_chunk(T, d_cq, d_model);
+  const int S = (d_model + kc - 1) / kc;
   float* part = static_cast<float*>(workspace);
   const long part_bytes = ((long)S * T * d_cq * 4 + 255) / 256 * 256;
   auto* c_q = reinterpret_cast<typename E::storage*>(static_cast<char*>(workspace) + part_bytes);
-  gemm<E>(h, w_dq, T, d_cq, d_model, S, false, part, d_cq, 0, nullptr, stream);
+  if constexpr (E::bytes == 2)
+    proj_bf16(h, T, d_model, kc, false,
+              ProjOut{static_cast<const uint16_t*>(w_dq), d_cq, part, d_cq, 0},
+              ProjOut{nullptr, 0, nullptr, 0, 0}, stream);
+  else
+    gemm_f32<E>(h, w_dq, T, d_cq, d_model, kc, false, part, d_cq, 0, nullptr, stream);
   hipLaunchKernelGGL(q_norm_kernel<E>, dim3(T), dim3(256), 0, stream, part, S, T, d_cq, q_gain,
                      eps, c_q);
-  gemm<E>(c_q, w_uq, T, n_h * D_H, d_cq, 1, true, nullptr, n_h * D_H, 0, q_nope, stream);
-  gemm<E>(c_q, w_qr, T, n_h * D_R, d_cq, 1, true, nullptr, n_h * D_R, 0, q_rope, stream);
+  if constexpr (E::bytes == 2) {
+    proj_bf16(c_q, T, d_cq, d_cq, true,
+              ProjOut{static_cast<const uint16_t*>(w_uq), n_h * D_H, q_nope, n_h * D_H, 0},
+              ProjOut{static_cast<const uint16_t*>(w_qr), n_h * D_R, q_rope, n_h * D_R, 0},
+              stream);
+  } else {
+    gemm_f32<E>(c_q, w_uq, T, n_h * D_H, d_cq, d_cq, true, nullptr, n_h * D_H, 0, q_nope, stream);
+    gemm_f32<E>(c_q, w_qr, T, n_h * D_R, d_cq, d_cq, true, nullptr, n_h * D_R, 0, q_rope, stream);
+  }
   return hipGetLastError();
 }
 

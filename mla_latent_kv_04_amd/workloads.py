@@ -37,6 +37,8 @@ D_H = 128       # per-head width d_h
 ROW = D_C + D_R # elements of one cached latent row
 BLOCK = 64      # tokens per paged block
 ROPE_BASE = 10000.0
+D_MODEL_V2 = 5120   # DeepSeek-V2 hidden width
+D_CQ_V2 = 1536      # DeepSeek-V2 query compression width d_c'
 
 
 @dataclasses.dataclass(frozen=True)
@@ -206,3 +208,43 @@ def make_problem(wl: Workload, *, B: Optional[int] = None, n_h: Optional[int] = 
 def softmax_scale() -> float:
     """1/sqrt(d_h + d_R): the width of the concatenated query/key of one head."""
     return 1.0 / math.sqrt(D_H + D_R)
+
+
+@dataclasses.dataclass
+class HiddenInputs:
+    """Hidden states of a step's tokens and the producer weights that turn
+    them into cache rows and queries (float32 values, bf16-exact for bf16)."""
+    h: np.ndarray        # [T, d_model]
+    w_dkv: np.ndarray    # [512, d_model]
+    kv_gain: np.ndarray  # [512] float32
+    w_kr: np.ndarray     # [64, d_model]
+    w_dq: np.ndarray     # [d_cq, d_model]
+    q_gain: np.ndarray   # [d_cq] float32
+    w_uq: np.ndarray     # [n_h * 128, d_cq]
+    w_qr: np.ndarray     # [n_h * 64, d_cq]
+
+
+def make_hidden(prob: Problem, d_model: int = D_MODEL_V2, d_cq: int = D_CQ_V2) -> HiddenInputs:
+    """Hidden states for the step's T tokens and random producer weights of the
+    DeepSeek-V2 widths (hidden 5120, query compression 1536: adg.csdn.net blog,
+    §3.1.1).
+
+    Recipe (its own ``Generator(PCG64(seed + 7919))``, draws in this order):
+    h ~ N(0, 1); W^DKV, W^KR, W^DQ ~ N(0, 1/d_model); W^UQ, W^QR ~ N(0, 1/d_cq);
+    the two RMSNorm gains 1 + 0.1 N(0, 1), float32.  Weights are stored
+    [d_out, d_in]; float draws are rounded to bf16 for bf16 workloads."""
+    wl = prob.wl
+    bf16 = wl.dtype == "bf16"
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 7919))
+    T, n_h = prob.T, wl.n_h
+    h = _normal(rng, (T, d_model), 1.0, bf16)
+    w_dkv = _normal(rng, (D_C, d_model), 1.0 / math.sqrt(d_model), bf16)
+    w_kr = _normal(rng, (D_R, d_model), 1.0 / math.sqrt(d_model), bf16)
+    w_dq = _normal(rng, (d_cq, d_model), 1.0 / math.sqrt(d_model), bf16)
+    w_uq = _normal(rng, (n_h * D_H, d_cq), 1.0 / math.sqrt(d_cq), bf16)
+    w_qr = _normal(rng, (n_h * D_R, d_cq), 1.0 / math.sqrt(d_cq), bf16)
+    kv_gain = (1.0 + 0.1 * rng.standard_normal(D_C)).astype(np.float32)
+    q_gain = (1.0 + 0.1 * rng.standard_normal(d_cq)).astype(np.float32)
+    return HiddenInputs(h=h, w_dkv=w_dkv, kv_gain=kv_gain, w_kr=w_kr, w_dq=w_dq, q_gain=q_gain,
+                        w_uq=w_uq, w_qr=w_qr)
+

@@ -117,7 +117,7 @@ def test_split_plan_rejects_negative_length():
 def test_producers_reject_bad_arguments_and_size_their_workspace(lib):
     ws = lib.mla_kv_produce_workspace
     assert ws(128, 5120) > 0 and ws(0, 5120) == 0
-    assert ws(128, 5121) == -1 and ws(-1, 5120) == -1 and ws(128, 16) == -1
+    assert ws(128, 5121) == -1 and ws(-1, 5120) == -1 and ws(128, 32) == -1
     assert ws(256, 5120) >= ws(128, 5120)
     need = ws(4, 64)
 
@@ -129,7 +129,7 @@ def test_producers_reject_bad_arguments_and_size_their_workspace(lib):
                                   a["eps"], a["base"], a["kv"], a["nb"], a["bs"], a["tab"],
                                   a["ns"], a["mb"], a["seq"], a["pos"], a["w"], a["wb"], None)
     assert kv(dt=3) == 4
-    assert kv(dm=48) == 2 and kv(bs=32) == 2 and kv(eps=-1.0) == 2 and kv(base=0.0) == 2
+    assert kv(dm=48) == 2 and kv(dm=96) == 2 and kv(bs=32) == 2 and kv(eps=-1.0) == 2 and kv(base=0.0) == 2
     assert kv(wb=need - 1) == 2                      # workspace too small
     assert kv(h=NULL) == 1 and kv(w=NULL) == 1
     assert kv(kv=MISALIGNED) == 3
@@ -147,7 +147,7 @@ def test_producers_reject_bad_arguments_and_size_their_workspace(lib):
                                  a["dq"], a["nh"], a["dt"], a["eps"], a["qn"], a["qr"], a["w"],
                                  a["wb"], None)
     assert q(dt=5) == 4
-    assert q(dq=40) == 2 and q(dq=4096) == 2 and q(nh=0) == 2 and q(wb=qneed - 1) == 2
+    assert q(dq=40) == 2 and q(dq=96) == 2 and q(dm=160) == 2 and q(dq=4096) == 2 and q(nh=0) == 2 and q(wb=qneed - 1) == 2
     assert q(wu=NULL) == 1
     assert q(wd=MISALIGNED) == 3
     assert q(T=0, h=NULL) == 0
