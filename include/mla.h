@@ -335,6 +335,41 @@ int32_t mla_q_produce(const void* h, const void* w_dq, const float* q_gain, cons
                       int32_t dtype, float eps, void* q_nope, void* q_rope, void* workspace,
                       int64_t workspace_bytes, void* stream);
 
+/*
+ * Non-absorbed chunked prefill: the literal form of eq. 7 (notes §2.1.1) with
+ * the per-head keys and values of eq. 10-11 (notes §2.1.2),
+ *   k^C_{j,i} = W^UK_i c^KV_j,  v^C_{j,i} = W^UV_i c^KV_j,
+ *   q_i = [q_nope_i ; R_{q_pos} q_rope_i],  k_{j,i} = [k^C_{j,i} ; k^R_j]
+ * (k^R_j as cached, already rotated; blog part 2 §2.2.2), softmax over the
+ * visible keys at `scale`, o_i = sum_j p_j v^C_{j,i}.  The blog keeps the
+ * absorbed form for generation; for a chunk of many query rows this form
+ * costs 2 (192 + 128) instead of 2 (576 + 512) flops per (row, head, key),
+ * plus the up-projection of each key once.
+ *
+ * Same problem as mla_absorb_q + mla_decode_paged + mla_out_proj for one
+ * chunk of q_len rows per sequence: q_nope [B * q_len, n_h, 128] and q_rope
+ * [B * q_len, n_h, 64] (before rotation) in bf16, q_pos device int32
+ * [B * q_len]; w_uk, w_uv bf16 [n_h, 128, 512]; the paged cache, block_table
+ * and block_size as for mla_decode_paged; seq_lens a HOST int32 array [B]
+ * (keys of each sequence; row m of sequence b sees keys
+ * j < seq_lens[b] - (q_len - 1 - m)).  Outputs: out fp32 [B * q_len, n_h, 128]
+ * (as mla_out_proj's), lse fp32 [B * q_len, n_h] (natural log; a row with no
+ * visible key gets out = 0 and lse = -inf).  A block id outside
+ * [0, num_blocks) contributes no keys.  bf16 only (else MLA_ERR_DTYPE).
+ * seq_lens[b] <= max_blocks * 64 and num_blocks * 64 * 1152 < 2^32 bytes
+ * (else MLA_ERR_SHAPE).  The workspace (caller-owned device memory of at
+ * least mla_prefill_mha_workspace(max seq_len, n_h) bytes) holds k^C and
+ * v^C of one sequence at a time; sequences run one after the other on the
+ * stream.
+ */
+int64_t mla_prefill_mha_workspace(int32_t max_seq_len, int32_t n_h);
+int32_t mla_prefill_mha(const void* q_nope, const void* q_rope, const int32_t* q_pos,
+                        const void* w_uk, const void* w_uv, const void* kv_cache,
+                        int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+                        int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t q_len,
+                        int32_t n_h, int32_t dtype, float scale, float rope_base, float* out,
+                        float* lse, void* workspace, int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@ _EXPORTS = ("mla_status_string", "mla_abi_version", "mla_kv_append", "mla_absorb
             "mla_decode_paged", "mla_splitkv_combine", "mla_out_proj", "mla_split_plan",
             "mla_plan_decode", "mla_decode_paged_planned", "mla_combine_planned",
             "mla_out_proj_planned", "mla_kv_produce_workspace", "mla_kv_produce",
-            "mla_q_produce_workspace", "mla_q_produce")
+            "mla_q_produce_workspace", "mla_q_produce", "mla_prefill_mha_workspace",
+            "mla_prefill_mha")
 
 
 class MLAError(RuntimeError):
@@ -72,6 +73,9 @@ def load() -> ctypes.CDLL:
         "mla_q_produce_workspace": (ctypes.c_int64, [_I, _I, _I, _I]),
         "mla_q_produce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P,
                                ctypes.c_int64, _P]),
+        "mla_prefill_mha_workspace": (ctypes.c_int64, [_I, _I]),
+        "mla_prefill_mha": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F,
+                                 _F, _P, _P, _P, ctypes.c_int64, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -416,3 +420,46 @@ def mla_q_produce(h, w_dq, q_gain, w_uq, w_qr, q_nope, q_rope, eps, workspace, s
         _dev(q_rope, "q_rope"), _dev(workspace, "workspace"), int(workspace.numel()),
         _stream(stream))
     _check("mla_q_produce", st)
+
+
+def mla_prefill_mha_workspace(max_seq_len, n_h):
+    """Workspace bytes of mla_prefill_mha (see mla.h)."""
+    n = int(load().mla_prefill_mha_workspace(int(max_seq_len), int(n_h)))
+    if n < 0:
+        raise ValueError("invalid sizes for mla_prefill_mha_workspace")
+    return n
+
+
+def mla_prefill_mha(q_nope, q_rope, q_pos, w_uk, w_uv, kv_cache, block_table, seq_lens, q_len,
+                    softmax_scale, rope_base, out, lse, workspace, stream=None):
+    """Non-absorbed chunked prefill (see mla.h).  seq_lens is a host array [B]."""
+    import numpy as np
+    torch = _torch()
+    dt = _dtype_code(q_nope)
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    B = int(lens.shape[0])
+    n_h = int(q_nope.shape[-2])
+    T = B * int(q_len)
+    if tuple(q_nope.shape) != (T, n_h, D_H) or tuple(q_rope.shape) != (T, n_h, D_R):
+        raise ValueError("q_nope must be [B*q_len, n_h, 128] and q_rope [B*q_len, n_h, 64]")
+    if tuple(w_uk.shape) != (n_h, D_H, D_C) or tuple(w_uv.shape) != (n_h, D_H, D_C):
+        raise ValueError("w_uk and w_uv must be [n_h, 128, 512]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    if out.numel() != T * n_h * D_H or lse.numel() != T * n_h:
+        raise ValueError("out must hold [B*q_len, n_h, 128] and lse [B*q_len, n_h]")
+    for name, t in (("q_rope", q_rope), ("w_uk", w_uk), ("w_uv", w_uv), ("kv_cache", kv_cache)):
+        if t.dtype != q_nope.dtype:
+            raise TypeError(f"{name} must have q_nope's dtype")
+    if workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    f32 = torch.float32
+    st = load().mla_prefill_mha(
+        _dev(q_nope, "q_nope"), _dev(q_rope, "q_rope"), _dev(q_pos, "q_pos", torch.int32),
+        _dev(w_uk, "w_uk"), _dev(w_uv, "w_uv"), _dev(kv_cache, "kv_cache"),
+        int(kv_cache.shape[0]), int(kv_cache.shape[1]),
+        _dev(block_table, "block_table", torch.int32), int(block_table.shape[1]),
+        lens.ctypes.data_as(ctypes.c_void_p), B, int(q_len), n_h, dt, float(softmax_scale),
+        float(rope_base), _dev(out, "out", f32), _dev(lse, "lse", f32),
+        _dev(workspace, "workspace"), int(workspace.numel()), _stream(stream))
+    _check("mla_prefill_mha", st)

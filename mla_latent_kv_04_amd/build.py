@@ -31,7 +31,7 @@ COMMON = [
 # exception: its value waves keep their accumulators in AGPRs (AGPR form).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 SOURCES = ["kv_append.hip", "absorb_q.hip", "decode.hip", "decode_h64.hip", "combine.hip", "out_proj.hip",
-           "produce.hip", "mla_api.cpp", "produce_api.cpp"]
+           "produce.hip", "prefill_mha.hip", "mla_api.cpp", "produce_api.cpp"]
 EXTRA = {src: VGPR_FORM for src in SOURCES if src.endswith(".hip") and src != "decode_h64.hip"}
 
 

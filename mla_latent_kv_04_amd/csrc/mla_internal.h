@@ -63,4 +63,14 @@ hipError_t launch_q_produce(const void* h, const void* w_dq, const float* q_gain
                             int n_h, int dtype, float eps, void* q_nope, void* q_rope,
                             void* workspace, hipStream_t stream);
 
+// Non-absorbed chunked prefill (prefill_mha.hip), bf16.  seq_lens is a host
+// array; the workspace holds k^C and v^C^T of the longest sequence.
+long prefill_mha_workspace(int max_len, int n_h);
+hipError_t launch_prefill_mha(const void* q_nope, const void* q_rope, const int* q_pos,
+                              const void* w_uk, const void* w_uv, const void* cache,
+                              int num_blocks, const int* table, int max_blocks,
+                              const int* seq_lens, int B, int q_len, int n_h, float scale,
+                              float base, float* out, float* lse, void* workspace,
+                              hipStream_t stream);
+
 }  // namespace mla

@@ -22,6 +22,7 @@
 
 #include "mla_common.h"
 #include "mla_internal.h"
+#include "proj_tile.h"
 
 namespace mla {
 
@@ -82,175 +83,6 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(const typename E::storage*
     } else {
       *reinterpret_cast<float4*>(part + ((long)z * T + t) * ldo + col0 + nb) =
           float4{acc[tb][0], acc[tb][1], acc[tb][2], acc[tb][3]};
-    }
-  }
-}
-
-// bf16 tiles ----------------------------------------------------------------
-constexpr int PN = 128;                        // W rows (outputs) per workgroup
-constexpr int PK = 64;                         // K slices are multiples of this
-
-// One direct global->LDS load: lane l's 16 bytes at base + lane_off land at
-// LDS byte lds_dst + 16 l (M0 holds the LDS address; one wait state before
-// the load reads it).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // M0 is named as clobbered on purpose
-__device__ __forceinline__ void dma16(unsigned lds_dst, const char* base, unsigned lane_off) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %2"
-      :
-      : "v"(lane_off), "s"(lds_dst), "s"(base)
-      : "m0");
-}
-#pragma clang diagnostic pop
-
-// Wait until at most VMC of this wave's vector-memory loads are in flight
-// and its LDS reads are done, then a workgroup barrier.
-template <int VMC>
-__device__ __forceinline__ void stage_barrier() {
-  static_assert(VMC >= 0 && VMC < 64, "vmcnt field");
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt((VMC & 15) | ((VMC >> 4) << 14) | 0x70);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// One projection of a bf16 launch: W [N, K]; DIRECT: bf16 out rows of ldo
-// elements, columns col0..; else fp32 partials part [S, T, ldo].
-struct ProjOut {
-  const uint16_t* W;
-  int N;
-  void* out;
-  int ldo;
-  int col0;
-};
-
-// Workgroup (x, y, z): W rows n0 .. n0 + 127 of projection p0 (x < tiles0)
-// or p1, X rows TT y .. TT y + TT - 1, K slice [z kc, min(K, (z + 1) kc)),
-// kc a multiple of KS.  Four waves in a 2 x 2 grid: wave (wn, wt) computes
-// W rows 64 wn.. against X rows TT/2 wt.. with 4 x TT/32 MFMA tiles.
-//
-// A stage holds KS of K: 128 + TT rows of 2 KS bytes (the W rows, then the
-// X rows); 16-byte piece q of stage row R sits in slot q ^ (R & 7), so that
-// the eight lanes of one ds_read_b128 phase (eight rows, one piece) hit
-// eight different bank groups.  Direct load i of a stage fills the 1024
-// bytes of rows RPI i .. RPI i + RPI - 1; wave w issues loads
-// w NIW .. w NIW + NIW - 1.  Rows past N or T re-read the last valid row;
-// their results are dropped.  NST stages are resident, NST - 1 in flight.
-template <bool DIRECT, int TT, int NST, int KS>
-__global__ void __launch_bounds__(256, (NST * (PN + TT) * KS * 2) <= 80 * 1024 ? 2 : 1)
-    proj_bf16_kernel(const uint16_t* __restrict__ X, int T, int K, int kc, ProjOut p0,
-                     ProjOut p1, int tiles0) {
-  constexpr int P_ROWB = KS * 2;               // bytes of one row in a stage
-  constexpr int SPR = P_ROWB / 16;             // 16-byte slots per row
-  constexpr int RPI = 64 / SPR;                // rows per direct load
-  constexpr int STAGE = (PN + TT) * P_ROWB;
-  constexpr int NIW = STAGE / 1024 / 4;
-  constexpr int TB = TT / 32;                  // MFMA row tiles of X per wave
-  static_assert(KS == 64 || KS == 128, "stage K");
-  __shared__ __attribute__((aligned(16))) char smem[NST * STAGE];
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const bool second = (int)blockIdx.x >= tiles0;
-  const ProjOut p = second ? p1 : p0;
-  const int n0 = ((int)blockIdx.x - (second ? tiles0 : 0)) * PN;
-  const int t0 = blockIdx.y * TT;
-  const int k0 = blockIdx.z * kc;
-  const int nst = (min(K, k0 + kc) - k0) / KS;
-
-  unsigned off[NIW];
-#pragma unroll
-  for (int j = 0; j < NIW; ++j) {
-    const int R = RPI * (wave * NIW + j) + lane / SPR;   // stage row
-    const int row = R < PN ? min(n0 + R, p.N - 1) : min(t0 + R - PN, T - 1);
-    off[j] = (unsigned)row * (unsigned)(K * 2) + (unsigned)(((lane % SPR) ^ (R & 7)) * 16);
-  }
-  const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
-  auto issue = [&](int s) __attribute__((always_inline)) {
-    const long kb = (long)(k0 + s * KS) * 2;
-    const char* wb = reinterpret_cast<const char*>(p.W) + kb;
-    const char* xb = reinterpret_cast<const char*>(X) + kb;
-    const unsigned dst = lds0 + (unsigned)((s % NST) * STAGE + wave * NIW * 1024);
-#pragma unroll
-    for (int j = 0; j < NIW; ++j)
-      dma16(dst + j * 1024, RPI * (wave * NIW + j) < PN ? wb : xb, off[j]);
-  };
-
-  // lane (g, r16) of MFMA tile (i, j) reads piece 4 ks + g of W row
-  // 64 wn + 16 i + r16 and of X row TT/2 wt + 16 j + r16
-  const int g = lane >> 4, r16 = lane & 15;
-  const int wn = wave & 1, wt = wave >> 1;
-  const int a_off = (64 * wn + r16) * P_ROWB, b_off = (PN + (TT / 2) * wt + r16) * P_ROWB;
-  f32x4_t acc[4][TB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < TB; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
-  auto compute = [&](int s) __attribute__((always_inline)) {
-    const char* st = smem + (s % NST) * STAGE;
-#pragma unroll
-    for (int ks = 0; ks < KS / 32; ++ks) {
-      const int sw = ((4 * ks + g) ^ (r16 & 7)) * 16;
-      i16x8_t a[4], b[TB];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const i16x8_t*>(st + a_off + 16 * i * P_ROWB + sw);
-#pragma unroll
-      for (int j = 0; j < TB; ++j)
-        b[j] = *reinterpret_cast<const i16x8_t*>(st + b_off + 16 * j * P_ROWB + sw);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16((bf16x8_t)a[i], (bf16x8_t)b[j],
-                                                              acc[i][j], 0, 0, 0);
-    }
-  };
-
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < nst) issue(s);
-  for (int s = 0; s < nst; ++s) {
-    // stage s landed: stages s + 1 .. min(s + NST - 2, nst - 1) stay in flight
-    const int ahead = min(NST - 2, nst - 1 - s);
-    if constexpr (NST == 4) {
-      if (ahead == 2)
-        stage_barrier<2 * NIW>();
-      else if (ahead == 1)
-        stage_barrier<NIW>();
-      else
-        stage_barrier<0>();
-    } else {
-      static_assert(NST == 3, "three or four stages");
-      if (ahead == 1)
-        stage_barrier<NIW>();
-      else
-        stage_barrier<0>();
-    }
-    if (s + NST - 1 < nst) issue(s + NST - 1);   // into the slot every wave finished with
-    compute(s);
-  }
-
-  // acc[i][j][e]: output n0 + 64 wn + 16 i + 4 g + e of row t0 + TT/2 wt + 16 j + r16
-#pragma unroll
-  for (int j = 0; j < TB; ++j) {
-    const int t = t0 + (TT / 2) * wt + 16 * j + r16;
-    if (t >= T) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + 64 * wn + 16 * i + 4 * g;
-      if (n >= p.N) continue;
-      if constexpr (DIRECT) {
-        uint16_t* o = static_cast<uint16_t*>(p.out) + (long)t * p.ldo + p.col0 + n;
-        *reinterpret_cast<uint2*>(o) = uint2{pack_bf16x2(acc[i][j][0], acc[i][j][1]),
-                                             pack_bf16x2(acc[i][j][2], acc[i][j][3])};
-      } else {
-        float* o = static_cast<float*>(p.out) + ((long)blockIdx.z * T + t) * p.ldo + p.col0 + n;
-        *reinterpret_cast<float4*>(o) = float4{acc[i][j][0], acc[i][j][1], acc[i][j][2],
-                                               acc[i][j][3]};
-      }
     }
   }
 }
@@ -405,16 +237,6 @@ __global__ void __launch_bounds__(256) q_norm_kernel(const float* __restrict__ p
   }
 }
 
-// Rows of X per bf16 workgroup: 128 (more reuse of each staged tile), or 64
-// for a projection so narrow that it splits K (twice the workgroups for the
-// same partial-sum bytes).  Measured on the decode shapes (T = 128): the
-// W^UQ + W^QR launch of 128 heads runs 8% faster with 128-row tiles, the
-// split W^DQ and W^DKV + W^KR ones 0-30% faster with 64.
-int t_tile(int T, int N) {
-  const long tiles128 = (long)((N + PN - 1) / PN) * ((T + 127) / 128);
-  return tiles128 < 128 ? 64 : 128;
-}
-
 // K slice length of a projection with N outputs for T rows: enough
 // workgroups to fill the chip (about 256), each slice a multiple of 64 and
 // at least 512 long, so that the fp32 partials it writes stay well below the
@@ -448,30 +270,6 @@ void gemm_f32(const void* X, const void* W, int T, int N, int K, int kc, bool di
                        (const Ts*)W, T, N, K, kc, part, ldo, col0, nullptr);
 }
 
-// bf16: the projections p0 and p1 (p1.N == 0: none) of X [T, K], one launch.
-void proj_bf16(const void* X, int T, int K, int kc, bool direct, ProjOut p0, ProjOut p1,
-               hipStream_t stream) {
-  const int tiles0 = (p0.N + PN - 1) / PN, tiles1 = (p1.N + PN - 1) / PN;
-  const int tt = t_tile(T, p0.N + p1.N);
-  dim3 grid(tiles0 + tiles1, (T + tt - 1) / tt, (K + kc - 1) / kc), block(256);
-  const auto* x = static_cast<const uint16_t*>(X);
-  if (tt == 64) {
-    if (direct)
-      hipLaunchKernelGGL((proj_bf16_kernel<true, 64, 3, 64>), grid, block, 0, stream, x, T, K, kc, p0,
-                         p1, tiles0);
-    else
-      hipLaunchKernelGGL((proj_bf16_kernel<false, 64, 3, 64>), grid, block, 0, stream, x, T, K, kc,
-                         p0, p1, tiles0);
-  } else {
-    if (direct)
-      hipLaunchKernelGGL((proj_bf16_kernel<true, 128, 4, 64>), grid, block, 0, stream, x, T, K, kc,
-                         p0, p1, tiles0);
-    else
-      hipLaunchKernelGGL((proj_bf16_kernel<false, 128, 4, 64>), grid, block, 0, stream, x, T, K, kc,
-                         p0, p1, tiles0);
-  }
-}
-
 template <class E>
 hipError_t kv_produce(const void* h, const void* w_dkv, const float* kv_gain, const void* w_kr,
                       int T, int d_model, float eps, float base, void* cache, int num_blocks,
@@ -483,9 +281,10 @@ hipError_t kv_produce(const void* h, const void* w_dkv, const float* kv_gain, co
   // the latent and the key projections fill columns 0..511 and 512..575 of
   // one partial buffer [S, T, 576]
   if constexpr (E::bytes == 2) {
-    proj_bf16(h, T, d_model, kc, false,
-              ProjOut{static_cast<const uint16_t*>(w_dkv), D_C, part, ROW, 0},
-              ProjOut{static_cast<const uint16_t*>(w_kr), D_R, part, ROW, D_C}, stream);
+    proj_bf16<OUT_PARTIAL>(XSrc{static_cast<const uint16_t*>(h), d_model, nullptr, 0}, T, d_model,
+                           kc, ProjOut{static_cast<const uint16_t*>(w_dkv), D_C, part, ROW, 0, 0},
+                           ProjOut{static_cast<const uint16_t*>(w_kr), D_R, part, ROW, D_C, 0},
+                           stream);
   } else {
     gemm_f32<E>(h, w_dkv, T, D_C, d_model, kc, false, part, ROW, 0, nullptr, stream);
     gemm_f32<E>(h, w_kr, T, D_R, d_model, kc, false, part, ROW, D_C, nullptr, stream);
@@ -506,18 +305,20 @@ hipError_t q_produce(const void* h, const void* w_dq, const float* q_gain, const
   const long part_bytes = ((long)S * T * d_cq * 4 + 255) / 256 * 256;
   auto* c_q = reinterpret_cast<typename E::storage*>(static_cast<char*>(workspace) + part_bytes);
   if constexpr (E::bytes == 2)
-    proj_bf16(h, T, d_model, kc, false,
-              ProjOut{static_cast<const uint16_t*>(w_dq), d_cq, part, d_cq, 0},
-              ProjOut{nullptr, 0, nullptr, 0, 0}, stream);
+    proj_bf16<OUT_PARTIAL>(XSrc{static_cast<const uint16_t*>(h), d_model, nullptr, 0}, T, d_model,
+                           kc, ProjOut{static_cast<const uint16_t*>(w_dq), d_cq, part, d_cq, 0, 0},
+                           ProjOut{nullptr, 0, nullptr, 0, 0, 0}, stream);
   else
     gemm_f32<E>(h, w_dq, T, d_cq, d_model, kc, false, part, d_cq, 0, nullptr, stream);
   hipLaunchKernelGGL(q_norm_kernel<E>, dim3(T), dim3(256), 0, stream, part, S, T, d_cq, q_gain,
                      eps, c_q);
   if constexpr (E::bytes == 2) {
-    proj_bf16(c_q, T, d_cq, d_cq, true,
-              ProjOut{static_cast<const uint16_t*>(w_uq), n_h * D_H, q_nope, n_h * D_H, 0},
-              ProjOut{static_cast<const uint16_t*>(w_qr), n_h * D_R, q_rope, n_h * D_R, 0},
-              stream);
+    proj_bf16<OUT_ROWS>(XSrc{reinterpret_cast<const uint16_t*>(c_q), d_cq, nullptr, 0}, T, d_cq, d_cq,
+                        ProjOut{static_cast<const uint16_t*>(w_uq), n_h * D_H, q_nope, n_h * D_H,
+                                0, 0},
+                        ProjOut{static_cast<const uint16_t*>(w_qr), n_h * D_R, q_rope, n_h * D_R,
+                                0, 0},
+                        stream);
   } else {
     gemm_f32<E>(c_q, w_uq, T, n_h * D_H, d_cq, d_cq, true, nullptr, n_h * D_H, 0, q_nope, stream);
     gemm_f32<E>(c_q, w_qr, T, n_h * D_R, d_cq, d_cq, true, nullptr, n_h * D_R, 0, q_rope, stream);

@@ -1,7 +1,8 @@
-// C ABI entry points of the producers (include/mla.h): host-side argument
-// checks, then launch.  As for the other entry points, every check runs
-// before anything is enqueued, and nothing is allocated, freed or
-// synchronised: the split-K partials and c^Q live in the caller's workspace.
+// C ABI entry points of the producers and of the non-absorbed prefill
+// (include/mla.h): host-side argument checks, then launch.  As for the other
+// entry points, every check runs before anything is enqueued, and nothing is
+// allocated, freed or synchronised: split-K partials, c^Q, and the prefill's
+// per-head keys and values live in the caller's workspace.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,6 +81,46 @@ int32_t mla_q_produce(const void* h, const void* w_dq, const float* q_gain, cons
   return hip_status(mla::launch_q_produce(h, w_dq, q_gain, w_uq, w_qr, T, d_model, d_cq, n_h,
                                           dtype, eps, q_nope, q_rope, workspace,
                                           (hipStream_t)stream));
+}
+
+int64_t mla_prefill_mha_workspace(int32_t max_seq_len, int32_t n_h) {
+  if (max_seq_len < 0 || n_h < 1 || n_h > 1024) return -1;
+  return mla::prefill_mha_workspace(max_seq_len, n_h);
+}
+
+int32_t mla_prefill_mha(const void* q_nope, const void* q_rope, const int32_t* q_pos,
+                        const void* w_uk, const void* w_uv, const void* kv_cache,
+                        int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+                        int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t q_len,
+                        int32_t n_h, int32_t dtype, float scale, float rope_base, float* out,
+                        float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (B < 0 || q_len < 0 || n_h < 1 || n_h > 1024 || block_size != MLA_BLOCK || max_blocks < 1 ||
+      num_blocks < 1 || !(scale > 0.0f) || !(rope_base > 0.0f))
+    return MLA_ERR_SHAPE;
+  if (B == 0 || q_len == 0) return MLA_OK;
+  if (!seq_lens) return MLA_ERR_NULL;
+  int32_t max_len = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (seq_lens[b] < 0 || (int64_t)seq_lens[b] > (int64_t)max_blocks * MLA_BLOCK)
+      return MLA_ERR_SHAPE;
+    max_len = seq_lens[b] > max_len ? seq_lens[b] : max_len;
+  }
+  // cache rows are addressed with 32-bit byte offsets
+  if ((int64_t)num_blocks * MLA_BLOCK * 576 * 2 >= (int64_t(1) << 32)) return MLA_ERR_SHAPE;
+  if (!fits_2g((int64_t)B * q_len * n_h, 192) || !fits_2g((int64_t)n_h * 128, 512))
+    return MLA_ERR_SHAPE;
+  if (workspace_bytes < mla::prefill_mha_workspace(max_len, n_h)) return MLA_ERR_SHAPE;
+  if (!q_nope || !q_rope || !q_pos || !w_uk || !w_uv || !kv_cache || !block_table || !out ||
+      !lse || !workspace)
+    return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(w_uv) ||
+      !aligned16(kv_cache) || !aligned16(out) || !aligned16(workspace) || !aligned4(lse))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_prefill_mha(q_nope, q_rope, q_pos, w_uk, w_uv, kv_cache,
+                                            num_blocks, block_table, max_blocks, seq_lens, B,
+                                            q_len, n_h, scale, rope_base, out, lse, workspace,
+                                            (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -172,6 +172,23 @@ def step(dp: DeviceProblem, stream=None):
         mla.mla_out_proj(dp.o_lat, dp.w_uv, dp.out, stream=stream)
 
 
+def prefill_workspace(dp: DeviceProblem):
+    """Device workspace for step_non_absorbed (k^C and v^C of the longest sequence)."""
+    torch = _torch()
+    n = mla.mla_prefill_mha_workspace(int(dp.prob.seq_lens.max()), dp.n_h)
+    return torch.empty(n, dtype=torch.uint8, device=dp.kv_cache.device)
+
+
+def step_non_absorbed(dp: DeviceProblem, workspace, stream=None):
+    """One pass of the chunked-prefill path in the non-absorbed form: append ->
+    per-head keys and values -> attention, into dp.out / dp.lse (bf16 only)."""
+    mla.mla_kv_append(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r, dp.new_seq,
+                      dp.new_pos, ROPE_BASE, stream=stream)
+    mla.mla_prefill_mha(dp.q_nope, dp.q_rope, dp.q_pos, dp.w_uk, dp.w_uv, dp.kv_cache,
+                        dp.block_table, dp.prob.seq_lens, dp.q_len, softmax_scale(), ROPE_BASE,
+                        dp.out, dp.lse, workspace, stream=stream)
+
+
 def _attend_planned(dp: DeviceProblem, stream=None):
     mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
                                  softmax_scale(), dp.work, dp.o_lat, dp.lse,

@@ -151,3 +151,32 @@ def test_producers_reject_bad_arguments_and_size_their_workspace(lib):
     assert q(wu=NULL) == 1
     assert q(wd=MISALIGNED) == 3
     assert q(T=0, h=NULL) == 0
+
+
+def test_prefill_mha_rejects_bad_arguments_and_sizes_its_workspace(lib):
+    import numpy as np
+    ws = lib.mla_prefill_mha_workspace
+    # k^C and v^C (hi + lo) of the longest sequence, rows padded to a multiple of 128
+    assert ws(8192, 128) == 3 * 128 * 128 * 8192 * 2
+    assert ws(1, 16) == ws(128, 16) == 3 * 16 * 128 * 128 * 2
+    assert ws(-1, 16) == -1 and ws(10, 0) == -1
+    lens = np.array([300, 200], dtype=np.int32)
+    need = ws(300, 16)
+
+    def pf(**kw):
+        a = dict(qn=FAKE, qr=FAKE, qp=FAKE, wk=FAKE, wv=FAKE, kv=FAKE, nb=16, bs=64, tab=FAKE,
+                 mb=8, lens=lens.ctypes.data, B=2, q=100, nh=16, dt=1, sc=0.07, base=1e4,
+                 out=FAKE, lse=FAKE, w=FAKE, wb=need)
+        a.update(kw)
+        return lib.mla_prefill_mha(a["qn"], a["qr"], a["qp"], a["wk"], a["wv"], a["kv"], a["nb"],
+                                   a["bs"], a["tab"], a["mb"], a["lens"], a["B"], a["q"], a["nh"],
+                                   a["dt"], a["sc"], a["base"], a["out"], a["lse"], a["w"],
+                                   a["wb"], None)
+    assert pf(dt=0) == 4                                  # bf16 only
+    assert pf(bs=32) == 2 and pf(nh=0) == 2 and pf(sc=0.0) == 2 and pf(base=-1.0) == 2
+    assert pf(mb=4) == 2                                  # 300 keys need 5 blocks of 64
+    assert pf(wb=need - 1) == 2
+    assert pf(nb=1 << 20) == 2                            # cache beyond 32-bit offsets
+    assert pf(lens=None) == 1 and pf(wk=NULL) == 1 and pf(lse=NULL) == 1
+    assert pf(out=MISALIGNED) == 3
+    assert pf(B=0, lens=None) == 0 and pf(q=0) == 0       # nothing to do
