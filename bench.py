@@ -83,6 +83,21 @@ def load_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def non_absorbed_flops(prob):
+    """FLOPs of one mla_prefill_mha call: the up-projections k^C = W^UK c^KV and
+    v^C = W^UV c^KV of every key (2 * 512 * 128 per key, head and matrix),
+    then 2 * 192 for the score and 2 * 128 for the weighted sum per visible
+    (query row, head, key)."""
+    wl = prob.wl
+    keys = int(sum(int(L) for L in prob.seq_lens))
+    pairs = 0
+    for b in range(wl.B):
+        L = int(prob.seq_lens[b])
+        q = wl.q_len
+        pairs += sum(max(0, L - (q - 1 - m)) for m in range(q))
+    return 2 * (2 * 512 * 128) * keys * wl.n_h + pairs * wl.n_h * (2 * 192 + 2 * 128)
+
+
 def producer_work(T, n_h, d_model, d_cq, esz):
     """(kv bytes, q bytes, kv flops, q flops) of the two producers for T tokens.
 
@@ -157,6 +172,9 @@ def main():
                     help="split-KV partitions per row; 0 = balanced work plan (default: workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attention", choices=("absorbed", "non-absorbed"), default="absorbed",
+                    help="chunked prefill only: non-absorbed = per-head keys and values, then "
+                         "attention (mla_prefill_mha)")
     ap.add_argument("--from-hidden", action="store_true",
                     help="start the step from hidden states: the cache-row and query producers "
                          "(DeepSeek-V2 widths) replace the append and the given queries")
@@ -178,6 +196,10 @@ def main():
                                                 make_hidden, make_problem, softmax_scale)
 
     wl = WORKLOADS[args.workload]
+    non_absorbed = args.attention == "non-absorbed"
+    if non_absorbed and (wl.q_len == 1 or wl.dtype != "bf16"):
+        print("--attention non-absorbed is for bf16 chunked prefill workloads", file=sys.stderr)
+        sys.exit(2)
     if args.from_hidden and wl.n_h != 128:
         print("--from-hidden uses the DeepSeek-V2 widths (128 heads, query compression); "
               f"{wl.name} has {wl.n_h} heads", file=sys.stderr)
@@ -204,7 +226,20 @@ def main():
                                  dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
 
+    pf_ws = pipeline.prefill_workspace(dp) if non_absorbed else None
+
     def one_step(ev=None):
+        if non_absorbed:
+            mla.mla_kv_append(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r, dp.new_seq,
+                              dp.new_pos, ROPE_BASE)
+            if ev is not None:
+                ev[0].record(stream)
+            mla.mla_prefill_mha(dp.q_nope, dp.q_rope, dp.q_pos, dp.w_uk, dp.w_uv, dp.kv_cache,
+                                dp.block_table, prob.seq_lens, dp.q_len, scale, ROPE_BASE,
+                                dp.out, dp.lse, pf_ws)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         if hw is None:
             mla.mla_kv_append(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r, dp.new_seq,
                               dp.new_pos, ROPE_BASE)
@@ -275,6 +310,8 @@ def main():
     value = tokens / (ms_per_step * 1e-3)
 
     by, fl = algorithmic_work(prob)
+    if non_absorbed:
+        fl = non_absorbed_flops(prob)
     compute_bound = wl.q_len > 1
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     gbs = by / (dec_ms * 1e-3) / 1e9
@@ -317,6 +354,7 @@ def main():
            "split_kv": ("balanced plan" if splits == 0 else f"{splits} per row"),
            "work_items": (int(dp.work.shape[0]) if splits == 0 else dp.B * dp.q_len * splits),
            "d_c": 512, "d_R": 64, "d_h": 128,
+           "attention_form": args.attention,
            "step_input": ("hidden states (cache-row and query producers in the step)"
                           if hw is not None else "new latent rows and per-head queries")}
     rec = {
@@ -326,7 +364,10 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": cfg, "roofline": roof,
-        "attention_kernel": {"us_per_launch": round(dec_ms * 1e3, 2),
+        "attention_kernel": {"scope": ("mla_prefill_mha: k^C and v^C projections, then the "
+                                       "attention kernel" if non_absorbed else
+                                       "the paged attention kernel"),
+                             "us_per_launch": round(dec_ms * 1e3, 2),
                              "algorithmic_bytes": by, "algorithmic_flops": fl,
                              "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                              "mfma_tflops": round(tflops, 1),

@@ -44,12 +44,20 @@ constexpr int BUF = OFF_VL + VTILE;      // 56 KB; two buffers in LDS
 constexpr int NDMA = BUF / 1024 / NW;    // direct loads per wave per tile (7)
 constexpr float NEG_BIG_P = -1.0e30f;    // finite "no key yet" running max
 
+__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+
 // LDS layouts: every row is a whole number of 16-byte pieces, and piece p of
-// row r sits in slot p ^ (r & 7), so that the eight lanes of one
-// ds_read_b128 phase (eight rows, one piece) hit eight bank groups.
+// row r sits in slot p ^ f(r), so that the eight lanes of one ds_read_b128
+// phase (eight rows, one piece) hit eight bank groups: f(r) = r & 7 for v^T
+// rows (dims, read 8 consecutive at a time), kswz(r) for key rows (read as
+// rows {0..3, 8..11} + 32 b + 4 c, see below).
 //   k^C row (key) of 256 bytes, k^R row of 128 bytes, v^T row (dim) of 128
-//   bytes whose piece p holds keys 8 p .. 8 p + 7 in the order the
-//   projection stores them (within 32 keys: 4 q + i, then 16 + 4 q + i).
+//   bytes whose piece p holds keys 8 p .. 8 p + 7.
+// Score MFMA block a (16 keys) takes as its row 4 q + i the key
+// 32 (a >> 1) + 8 q + 4 (a & 1) + i of the tile: lane (g, r16) then holds
+// the scores of keys 32 (a >> 1) + 8 g + 4 (a & 1) + i, so that its eight P
+// values of PV k-step ks2 (blocks 2 ks2, 2 ks2 + 1) are keys
+// 32 ks2 + 8 g .. + 7, which is piece 4 ks2 + g of a v^T row.
 // Direct load I (0..55) of a tile fills LDS bytes [1024 I, 1024 I + 1024) of
 // the buffer: I < 16 k^C rows 4 I.., I < 24 k^R rows 8 (I - 16).., then v^T
 // hi rows and v^T lo rows 8 (I - 24) % 128..; wave w issues I = 7 w .. 7 w + 6.
@@ -111,10 +119,10 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
     const int I = NDMA * wave + j;
     if (I < 16) {                                         // k^C: 4 rows of 256 bytes
       const int r = 4 * I + (lane >> 4);
-      loff[j] = (unsigned)(r * (D_H * 2) + (((lane & 15) ^ (r & 7)) * 16));
+      loff[j] = (unsigned)(r * (D_H * 2) + (((lane & 15) ^ kswz(r)) * 16));
     } else if (I < 24) {                                  // k^R: 8 cache rows, bytes 1024..1151
       const int r = 8 * (I - 16) + (lane >> 3);
-      loff[j] = (unsigned)(r * (ROW * 2) + (((lane & 7) ^ (r & 7)) * 16));
+      loff[j] = (unsigned)(r * (ROW * 2) + (((lane & 7) ^ kswz(r)) * 16));
     } else {                                              // v^T hi / lo: 8 dims of 128 bytes
       const int d = 8 * ((I - 24) & 15) + (lane >> 3);
       loff[j] = (unsigned)(d * Lpad * 2 + (((lane & 7) ^ (d & 7)) * 16));
@@ -153,7 +161,6 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
 #pragma unroll
   for (int qq = 0; qq < 2; ++qq) lim[qq] = min(L, shift + mw + 16 * qq + r16);
 
-  const int sw = r16 & 7;
   if (ntiles > 0) issue(0, 0);
   for (int kt = 0; kt < ntiles; ++kt) {
     const int buf = kt & 1;
@@ -165,7 +172,8 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
     if (blk < 0 || blk >= num_blocks) continue;
     const char* tb = smem + buf * BUF;
     const int key0 = kt * KT;
-    // S^T[key][row]: s[a][qq] lane (g, r16) holds keys key0 + 16 a + 4 g + i
+    // S^T[key][row]: s[a][qq] lane (g, r16) holds keys
+    // key0 + 32 (a >> 1) + 8 g + 4 (a & 1) + i
     f32x4_t s[4][2];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -175,9 +183,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
     for (int ks = 0; ks < 6; ++ks) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int r = 16 * a + r16;
-        const char* kp = ks < 4 ? tb + OFF_KC + r * (D_H * 2) + (((4 * ks + g) ^ sw) * 16)
-                                : tb + OFF_KR + r * (D_R * 2) + (((4 * (ks - 4) + g) ^ sw) * 16);
+        const int r = 32 * (a >> 1) + 8 * (r16 >> 2) + 4 * (a & 1) + (r16 & 3);
+        const char* kp = ks < 4 ? tb + OFF_KC + r * (D_H * 2) + (((4 * ks + g) ^ kswz(r)) * 16)
+                                : tb + OFF_KR + r * (D_R * 2) + (((4 * (ks - 4) + g) ^ kswz(r)) * 16);
         const i16x8_t kf = *reinterpret_cast<const i16x8_t*>(kp);
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq)
@@ -185,9 +193,10 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
                                                              s[a][qq], 0, 0, 0);
       }
     }
-    // online softmax per query row; P (bf16) for the PV product, keys of
-    // PV k-step ks2 in the order the lane holds them: 32 ks2 + 4 g + i, then
-    // 32 ks2 + 16 + 4 g + i (the order of v^T's piece 4 ks2 + g)
+    // online softmax per query row (the running max moves with every larger
+    // score: the key that sets it then gets P = 1 exactly; a lazier max,
+    // moved only past a threshold, measurably raised the largest bf16 error).
+    // P (bf16) for the PV product: keys 32 ks2 + 8 g .. + 7 of k-step ks2.
     i16x8_t pf[2][2];
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
@@ -196,7 +205,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 16 * a + 4 * g + i;
+          const int key = key0 + 32 * (a >> 1) + 8 * g + 4 * (a & 1) + i;
           const float v = key < lim[qq] ? s[a][qq][i] * scale_log2 : -INFINITY;
           s[a][qq][i] = v;
           tmax = fmaxf(tmax, v);
@@ -225,7 +234,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const int vo = (16 * db + r16) * (KT * 2) + (((4 * ks2 + g) ^ sw) * 16);
+        const int vo = (16 * db + r16) * (KT * 2) + (((4 * ks2 + g) ^ (r16 & 7)) * 16);
 #pragma unroll
         for (int part = 0; part < 2; ++part) {
           const i16x8_t vf = *reinterpret_cast<const i16x8_t*>(tb + (part ? OFF_VL : OFF_VH) + vo);
@@ -275,15 +284,17 @@ hipError_t launch_prefill_mha(const void* q_nope, const void* q_rope, const int*
     uint16_t* vt = kc + (long)n_h * D_H * lpad;
     const int* trow = table + (long)b * max_blocks;
     if (L > 0) {
+      // 64-row tiles: two workgroups per CU (the reduction is only 512 long,
+      // so each workgroup's pipeline is short); measured 10% faster for k^C
       const XSrc x{cache16, ROW, trow, num_blocks};
       proj_bf16<OUT_HEADS>(x, L, D_C, D_C,
                            ProjOut{static_cast<const uint16_t*>(w_uk), n_h * D_H, kc, D_H, 0,
                                    (long)lpad * D_H},
-                           ProjOut{nullptr, 0, nullptr, 0, 0, 0}, stream);
+                           ProjOut{nullptr, 0, nullptr, 0, 0, 0}, stream, 64);
       proj_bf16<OUT_HEADS_T>(x, L, D_C, D_C,
                              ProjOut{static_cast<const uint16_t*>(w_uv), n_h * D_H, vt, lpad, 0,
                                      (long)D_H * lpad, (long)n_h * D_H * lpad},
-                             ProjOut{nullptr, 0, nullptr, 0, 0, 0}, stream);
+                             ProjOut{nullptr, 0, nullptr, 0, 0, 0}, stream, 64);
     }
     if (q_len == 0) continue;
     hipLaunchKernelGGL(mha_prefill_kernel, dim3((q_len + QB - 1) / QB, n_h), dim3(64 * NW), 0,

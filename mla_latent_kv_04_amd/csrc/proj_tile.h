@@ -53,14 +53,10 @@ struct XSrc {
 //   OUT_ROWS     bf16 out[t * ldo + col0 + n]
 //   OUT_PARTIAL  fp32 out[(z * T + t) * ldo + col0 + n], z the K slice
 //   OUT_HEADS    bf16 out[(n / 128) * hstride + t * 128 + n % 128]
-//   OUT_HEADS_T  bf16 out[(n / 128) * hstride + (n % 128) * ldo + perm(t)],
-//                every t of the workgroup's tile (rows past T repeat row
-//                T - 1's values, so the padding stays finite); with lo != 0
-//                the value is split into bf16 hi + lo, lo stored lo elements
-//                further.  perm reorders each aligned group of 32 rows:
-//                row 16 c + 4 q + i (c < 2, q < 4, i < 4) goes to 8 q + 4 c + i,
-//                so that the 8 rows an MFMA lane needs as one k-group (i < 4,
-//                c < 2) are contiguous
+//   OUT_HEADS_T  bf16 out[(n / 128) * hstride + (n % 128) * ldo + t], every t
+//                of the workgroup's tile (rows past T repeat row T - 1's
+//                values, so the padding stays finite); with lo != 0 the value
+//                is split into bf16 hi + lo, lo stored lo elements further
 enum { OUT_ROWS = 0, OUT_PARTIAL = 1, OUT_HEADS = 2, OUT_HEADS_T = 3 };
 
 struct ProjOut {
@@ -203,8 +199,7 @@ __global__ void __launch_bounds__(256, (NST * (PN + TT) * KS * 2) <= 80 * 1024 ?
                     (long)(n & 127) * p.ldo;
 #pragma unroll
       for (int j = 0; j < TB; ++j) {
-        const int t0j = t0 + (TT / 2) * wt + 16 * j + 4 * g;   // a multiple of 4
-        const int t = (t0j & ~31) | (((t0j >> 2) & 3) << 3) | (((t0j >> 4) & 1) << 2);
+        const int t = t0 + (TT / 2) * wt + 16 * j + 4 * g;
         *reinterpret_cast<uint2*>(o + t) = uint2{pack_bf16x2(acc[i][j][0], acc[i][j][1]),
                                                  pack_bf16x2(acc[i][j][2], acc[i][j][3])};
         if (p.lo != 0) {
@@ -255,9 +250,10 @@ inline int t_tile(int T, int N) {
 // bf16: the projections p0 and p1 (p1.N == 0: none) of X [T, K] rows, one
 // launch; OUTM as in proj_bf16_kernel.
 template <int OUTM>
-void proj_bf16(XSrc X, int T, int K, int kc, ProjOut p0, ProjOut p1, hipStream_t stream) {
+void proj_bf16(XSrc X, int T, int K, int kc, ProjOut p0, ProjOut p1, hipStream_t stream,
+               int tt_force = 0) {
   const int tiles0 = (p0.N + PN - 1) / PN, tiles1 = (p1.N + PN - 1) / PN;
-  const int tt = t_tile(T, p0.N + p1.N);
+  const int tt = tt_force ? tt_force : t_tile(T, p0.N + p1.N);
   dim3 grid(tiles0 + tiles1, (T + tt - 1) / tt, (K + kc - 1) / kc), block(256);
   if (tt == 64)
     hipLaunchKernelGGL((proj_bf16_kernel<OUTM, 64, 3, 64>), grid, block, 0, stream, X, T, K, kc,
