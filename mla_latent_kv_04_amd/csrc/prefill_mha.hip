@@ -198,6 +198,9 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
     // moved only past a threshold, measurably raised the largest bf16 error).
     // P (bf16) for the PV product: keys 32 ks2 + 8 g .. + 7 of k-step ks2.
     i16x8_t pf[2][2];
+    // the wave's first row sees the fewest keys: if it sees the whole tile,
+    // every row does and the tile needs no mask
+    const bool full = key0 + KT <= min(L, shift + mw);
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
       float tmax = -INFINITY;
@@ -206,14 +209,12 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = key0 + 32 * (a >> 1) + 8 * g + 4 * (a & 1) + i;
-          const float v = key < lim[qq] ? s[a][qq][i] * scale_log2 : -INFINITY;
+          const float v = full || key < lim[qq] ? s[a][qq][i] * scale_log2 : -INFINITY;
           s[a][qq][i] = v;
           tmax = fmaxf(tmax, v);
         }
       tmax = group4_max(tmax);
       const float m_new = fmaxf(m_run[qq], tmax);
-      const float alpha = fast_exp2(m_run[qq] - m_new);
-      m_run[qq] = m_new;
       float psum = 0.0f;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
@@ -223,11 +224,18 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
           psum += bf16_to_f32(pb);
           pf[qq][a >> 1][4 * (a & 1) + i] = (short)pb;
         }
-      l_run[qq] = l_run[qq] * alpha + psum;
+      // rescale only when some row of the wave has a new maximum (otherwise
+      // every factor is exactly 1)
+      if (__any(m_new > m_run[qq])) {
+        const float alpha = fast_exp2(m_run[qq] - m_new);
+        l_run[qq] *= alpha;
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+        for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[db][qq][e] *= alpha;
+          for (int e = 0; e < 4; ++e) acc[db][qq][e] *= alpha;
+      }
+      m_run[qq] = m_new;
+      l_run[qq] += psum;
     }
     // O^T[d][row] += (v^T hi + v^T lo)[d][keys] P[row][keys]
 #pragma unroll
