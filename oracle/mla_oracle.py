@@ -39,6 +39,9 @@ Readings where the pages are silent or garbled:
      stored as written in eq. 9 / 12, [d_out, d_model]; W^UQ and W^QR as
      [n_h * d_h, d_c'] and [n_h * d_R, d_c'], head i owning rows i*d_h.. and
      i*d_R.. respectively.
+  R10 a model that does not compress its queries (V2-Lite: blog, the V2-Lite
+     paragraph) projects both query parts straight from the hidden state,
+     q^C = W^QC h (eq. 1's W^Q, per-head rows) and q^R = W^QR h.
 """
 from __future__ import annotations
 
@@ -314,3 +317,18 @@ def q_produce(h, w_dq, q_gain, w_uq, w_qr, n_h: int, eps: float):
     q_nope = (c_q @ np.asarray(w_uq, F64).T).reshape(T, n_h, -1)
     q_rope = (c_q @ np.asarray(w_qr, F64).T).reshape(T, n_h, -1)
     return c_q, q_nope, q_rope
+
+
+def q_produce_direct(h, w_qc, w_qr, n_h: int):
+    """Per-head queries of a model without query compression (reading R10).
+
+    q^C_t = W^QC h_t  (eq. 1's q = W^Q h, split into heads of d_h)
+    q^R_t = W^QR h_t  (blog §2.2.2 with h in place of c^Q), before rotation
+    Returns (q_nope [T, n_h, d_h], q_rope [T, n_h, d_R]).
+    """
+    h = np.asarray(h, F64)
+    T = h.shape[0]
+    q_nope = (h @ np.asarray(w_qc, F64).T).reshape(T, n_h, -1)
+    q_rope = (h @ np.asarray(w_qr, F64).T).reshape(T, n_h, -1)
+    return q_nope, q_rope
+

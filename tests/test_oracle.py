@@ -385,3 +385,33 @@ def test_producers_match_scalar_loops():
             for d in range(d_r):
                 want = sum(w_qr[head * d_r + d][j] * cql[j] for j in range(d_cq))
                 assert abs(qr[t][head][d] - want) < 1e-12
+
+
+def test_direct_query_producer_matches_scalar_loops():
+    """q_produce_direct (reading R10) against element-by-element sums on a
+    tiny non-square shape, and against q_produce when the compression is an
+    identity without its norm (a transposed weight or a wrong head split
+    fails one of them)."""
+    rng = np.random.default_rng(11)
+    T, d_model, n_h, d_h, d_r = 3, 5, 2, 4, 3
+    h = rng.standard_normal((T, d_model))
+    w_qc = rng.standard_normal((n_h * d_h, d_model))
+    w_qr = rng.standard_normal((n_h * d_r, d_model))
+    qn, qr = orc.q_produce_direct(h, w_qc, w_qr, n_h)
+    assert qn.shape == (T, n_h, d_h) and qr.shape == (T, n_h, d_r)
+    for t in range(T):
+        for head in range(n_h):
+            for d in range(d_h):
+                want = sum(w_qc[head * d_h + d][j] * h[t][j] for j in range(d_model))
+                assert abs(qn[t][head][d] - want) < 1e-12
+            for d in range(d_r):
+                want = sum(w_qr[head * d_r + d][j] * h[t][j] for j in range(d_model))
+                assert abs(qr[t][head][d] - want) < 1e-12
+    # q_produce with W^DQ = I and a huge eps scaled back by the gain is the
+    # direct producer: RMSNorm(x) = g x / sqrt(mean(x^2) + eps) -> x when
+    # g = sqrt(eps) and eps >> mean(x^2)
+    eps = 1e20
+    _, qn2, qr2 = orc.q_produce(h, np.eye(d_model), np.full(d_model, np.sqrt(eps)), w_qc, w_qr,
+                                n_h, eps)
+    np.testing.assert_allclose(qn2, qn, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(qr2, qr, rtol=1e-9, atol=1e-9)
