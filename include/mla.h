@@ -336,6 +336,18 @@ int32_t mla_q_produce(const void* h, const void* w_dq, const float* q_gain, cons
                       int64_t workspace_bytes, void* stream);
 
 /*
+ * mla_q_produce_direct - per-head queries of T tokens for a model that does
+ * not compress its queries (DeepSeek-V2-Lite: blog, the V2-Lite paragraph):
+ *   q_nope = W^QC h -> [T, n_h, 128] (eq. 1's W^Q, head i owning rows i*128..),
+ *   q_rope = W^QR h -> [T, n_h, 64] (before rotation; head i rows i*64..).
+ * w_qc [n_h * 128, d_model], w_qr [n_h * 64, d_model], h [T, d_model], all
+ * in dtype; fp32 accumulation.  No workspace.  d_model a multiple of 64.
+ */
+int32_t mla_q_produce_direct(const void* h, const void* w_qc, const void* w_qr, int32_t T,
+                             int32_t d_model, int32_t n_h, int32_t dtype, void* q_nope,
+                             void* q_rope, void* stream);
+
+/*
  * Non-absorbed chunked prefill: the literal form of eq. 7 (notes §2.1.1) with
  * the per-head keys and values of eq. 10-11 (notes §2.1.2),
  *   k^C_{j,i} = W^UK_i c^KV_j,  v^C_{j,i} = W^UV_i c^KV_j,

@@ -22,8 +22,8 @@ _EXPORTS = ("mla_status_string", "mla_abi_version", "mla_kv_append", "mla_absorb
             "mla_decode_paged", "mla_splitkv_combine", "mla_out_proj", "mla_split_plan",
             "mla_plan_decode", "mla_decode_paged_planned", "mla_combine_planned",
             "mla_out_proj_planned", "mla_kv_produce_workspace", "mla_kv_produce",
-            "mla_q_produce_workspace", "mla_q_produce", "mla_prefill_mha_workspace",
-            "mla_prefill_mha")
+            "mla_q_produce_workspace", "mla_q_produce", "mla_q_produce_direct",
+            "mla_prefill_mha_workspace", "mla_prefill_mha")
 
 
 class MLAError(RuntimeError):
@@ -73,6 +73,7 @@ def load() -> ctypes.CDLL:
         "mla_q_produce_workspace": (ctypes.c_int64, [_I, _I, _I, _I]),
         "mla_q_produce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P,
                                ctypes.c_int64, _P]),
+        "mla_q_produce_direct": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
         "mla_prefill_mha_workspace": (ctypes.c_int64, [_I, _I]),
         "mla_prefill_mha": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F,
                                  _F, _P, _P, _P, ctypes.c_int64, _P]),
@@ -463,3 +464,21 @@ def mla_prefill_mha(q_nope, q_rope, q_pos, w_uk, w_uv, kv_cache, block_table, se
         float(rope_base), _dev(out, "out", f32), _dev(lse, "lse", f32),
         _dev(workspace, "workspace"), int(workspace.numel()), _stream(stream))
     _check("mla_prefill_mha", st)
+
+
+def mla_q_produce_direct(h, w_qc, w_qr, q_nope, q_rope, stream=None):
+    """Per-head queries straight from hidden states (no query compression; see mla.h)."""
+    dt = _dtype_code(h)
+    T, d_model = int(h.shape[0]), int(h.shape[1])
+    n_h = int(q_nope.shape[1])
+    if tuple(w_qc.shape) != (n_h * D_H, d_model) or tuple(w_qr.shape) != (n_h * D_R, d_model):
+        raise ValueError("w_qc must be [n_h*128, d_model] and w_qr [n_h*64, d_model]")
+    if tuple(q_nope.shape) != (T, n_h, D_H) or tuple(q_rope.shape) != (T, n_h, D_R):
+        raise ValueError("q_nope must be [T, n_h, 128] and q_rope [T, n_h, 64]")
+    for name, t in (("w_qc", w_qc), ("w_qr", w_qr), ("q_nope", q_nope), ("q_rope", q_rope)):
+        if t.dtype != h.dtype:
+            raise TypeError(f"{name} must have h's dtype")
+    st = load().mla_q_produce_direct(_dev(h, "h"), _dev(w_qc, "w_qc"), _dev(w_qr, "w_qr"), T,
+                                     d_model, n_h, dt, _dev(q_nope, "q_nope"),
+                                     _dev(q_rope, "q_rope"), _stream(stream))
+    _check("mla_q_produce_direct", st)

@@ -63,6 +63,10 @@ hipError_t launch_q_produce(const void* h, const void* w_dq, const float* q_gain
                             int n_h, int dtype, float eps, void* q_nope, void* q_rope,
                             void* workspace, hipStream_t stream);
 
+hipError_t launch_q_produce_direct(const void* h, const void* w_qc, const void* w_qr, int T,
+                                   int d_model, int n_h, int dtype, void* q_nope, void* q_rope,
+                                   hipStream_t stream);
+
 // Non-absorbed chunked prefill (prefill_mha.hip), bf16.  seq_lens is a host
 // array; the workspace holds k^C and v^C^T of the longest sequence.
 long prefill_mha_workspace(int max_len, int n_h);

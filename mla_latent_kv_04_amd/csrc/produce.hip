@@ -326,7 +326,36 @@ hipError_t q_produce(const void* h, const void* w_dq, const float* q_gain, const
   return hipGetLastError();
 }
 
+// Queries of a model without query compression: q^C = W^QC h, q^R = W^QR h
+// (both straight from the hidden states), one launch in bf16.
+template <class E>
+hipError_t q_direct(const void* h, const void* w_qc, const void* w_qr, int T, int d_model,
+                    int n_h, void* q_nope, void* q_rope, hipStream_t stream) {
+  if constexpr (E::bytes == 2) {
+    proj_bf16<OUT_ROWS>(XSrc{static_cast<const uint16_t*>(h), d_model, nullptr, 0}, T, d_model,
+                        d_model,
+                        ProjOut{static_cast<const uint16_t*>(w_qc), n_h * D_H, q_nope, n_h * D_H,
+                                0, 0},
+                        ProjOut{static_cast<const uint16_t*>(w_qr), n_h * D_R, q_rope, n_h * D_R,
+                                0, 0},
+                        stream);
+  } else {
+    gemm_f32<E>(h, w_qc, T, n_h * D_H, d_model, d_model, true, nullptr, n_h * D_H, 0, q_nope,
+                stream);
+    gemm_f32<E>(h, w_qr, T, n_h * D_R, d_model, d_model, true, nullptr, n_h * D_R, 0, q_rope,
+                stream);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_q_produce_direct(const void* h, const void* w_qc, const void* w_qr, int T,
+                                   int d_model, int n_h, int dtype, void* q_nope, void* q_rope,
+                                   hipStream_t stream) {
+  if (dtype == 1) return q_direct<BF16>(h, w_qc, w_qr, T, d_model, n_h, q_nope, q_rope, stream);
+  return q_direct<F32>(h, w_qc, w_qr, T, d_model, n_h, q_nope, q_rope, stream);
+}
 
 long kv_produce_workspace(int T, int d_model) {
   return (long)k_slices(T, ROW, d_model) * T * ROW * 4;

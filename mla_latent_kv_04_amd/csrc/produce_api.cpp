@@ -83,6 +83,23 @@ int32_t mla_q_produce(const void* h, const void* w_dq, const float* q_gain, cons
                                           (hipStream_t)stream));
 }
 
+int32_t mla_q_produce_direct(const void* h, const void* w_qc, const void* w_qr, int32_t T,
+                             int32_t d_model, int32_t n_h, int32_t dtype, void* q_nope,
+                             void* q_rope, void* stream) {
+  if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  if (T < 0 || d_model < 64 || d_model % 64 != 0 || n_h < 1 || n_h > 1024) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!fits_2g(T, d_model) || !fits_2g((int64_t)n_h * 128, d_model) ||
+      !fits_2g((int64_t)T * n_h, 128))
+    return MLA_ERR_SHAPE;
+  if (!h || !w_qc || !w_qr || !q_nope || !q_rope) return MLA_ERR_NULL;
+  if (!aligned16(h) || !aligned16(w_qc) || !aligned16(w_qr) || !aligned16(q_nope) ||
+      !aligned16(q_rope))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_q_produce_direct(h, w_qc, w_qr, T, d_model, n_h, dtype, q_nope,
+                                                 q_rope, (hipStream_t)stream));
+}
+
 int64_t mla_prefill_mha_workspace(int32_t max_seq_len, int32_t n_h) {
   if (max_seq_len < 0 || n_h < 1 || n_h > 1024) return -1;
   return mla::prefill_mha_workspace(max_seq_len, n_h);

@@ -51,6 +51,7 @@ __all__ = [
     "rope_rotate", "mla_attention_naive", "kv_cache_rows", "absorb_query",
     "latent_attention", "split_ranges", "combine_splits", "out_projection",
     "visible_keys", "mla_reference_problem", "rms_norm", "kv_produce", "q_produce",
+    "q_produce_direct",
 ]
 
 F64 = np.float64

@@ -180,3 +180,16 @@ def test_prefill_mha_rejects_bad_arguments_and_sizes_its_workspace(lib):
     assert pf(lens=None) == 1 and pf(wk=NULL) == 1 and pf(lse=NULL) == 1
     assert pf(out=MISALIGNED) == 3
     assert pf(B=0, lens=None) == 0 and pf(q=0) == 0       # nothing to do
+
+
+def test_direct_query_producer_rejects_bad_arguments(lib):
+    def q(**kw):
+        a = dict(h=FAKE, wc=FAKE, wr=FAKE, T=4, dm=64, nh=2, dt=1, qn=FAKE, qr=FAKE)
+        a.update(kw)
+        return lib.mla_q_produce_direct(a["h"], a["wc"], a["wr"], a["T"], a["dm"], a["nh"],
+                                        a["dt"], a["qn"], a["qr"], None)
+    assert q(dt=9) == 4
+    assert q(dm=96) == 2 and q(nh=0) == 2 and q(T=-1) == 2
+    assert q(wr=NULL) == 1 and q(qn=NULL) == 1
+    assert q(qr=MISALIGNED) == 3
+    assert q(T=0, h=NULL) == 0

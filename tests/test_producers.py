@@ -121,6 +121,36 @@ def test_q_produce_matches_oracle(dtype, d_model, d_cq, n_h):
         assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + rms * 2.0 ** -9)
 
 
+@pytest.mark.parametrize("dtype,d_model,n_h", [("bf16", 2048, 16), ("f32", 256, 2)])
+def test_direct_query_producer_matches_oracle(dtype, d_model, n_h):
+    """Queries of a model without query compression (V2-Lite's widths in
+    bf16: hidden 2048, 16 heads)."""
+    import torch
+    from mla_latent_kv_04_amd import _binding as mla
+    rng = np.random.default_rng(d_model + n_h)
+    T = 150                                           # two 128-row tiles, the second ragged
+    h = rng.standard_normal((T, d_model)).astype(np.float32)
+    if dtype == "bf16":
+        h = round_to_bf16(h)
+    w_qc = _weights(rng, (n_h * D_H, d_model), d_model, dtype)
+    w_qr = _weights(rng, (n_h * D_R, d_model), d_model, dtype)
+    ref_n, ref_r = orc.q_produce_direct(h, w_qc, w_qr, n_h)
+    say(f"q_produce_direct {dtype} d_model={d_model} n_h={n_h}")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q_nope = torch.empty((T, n_h, D_H), dtype=tdt, device="cuda")
+    q_rope = torch.empty((T, n_h, D_R), dtype=tdt, device="cuda")
+    mla.mla_q_produce_direct(_dev(h, dtype), _dev(w_qc, dtype), _dev(w_qr, dtype), q_nope, q_rope)
+    torch.cuda.synchronize()
+    for got, ref in ((q_nope, ref_n), (q_rope, ref_r)):
+        g = got.float().cpu().numpy().astype(np.float64)
+        if dtype == "bf16":
+            # fp32 products, one rounding of each output
+            rms = np.sqrt(np.mean(ref ** 2))
+            assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -8 + rms * 1e-4)
+        else:
+            assert rel_err(g, ref) <= 1e-5
+
+
 def test_hidden_states_to_attention_output():
     """Cache rows and the query produced from hidden states, then absorb,
     attention and out-projection, against the oracle's producers followed by
