@@ -128,3 +128,55 @@ def test_prefill_mha_full_size_sampled():
     ref, _, _ = oracle_sequence(prob, 0, heads=heads, rows=rows)
     assert rel_err(out[np.asarray(rows)][:, heads], ref) <= TOL["bf16"]
     assert np.isfinite(out).all()
+
+
+@pytest.mark.parametrize("L,q,n_h", [(40, 64, 3), (0, 16, 2), (130, 130, 5)])
+def test_prefill_mha_rows_without_keys_and_odd_head_counts(L, q, n_h):
+    """Inputs built directly: a chunk longer than its sequence (its first
+    q - L rows see no key: out 0, lse -inf, reading R6), an empty sequence,
+    and head counts that fill no 16-head block."""
+    import torch
+    from mla_latent_kv_04_amd import _binding as mla
+    from mla_latent_kv_04_amd.workloads import D_C, D_H, D_R, ROW, round_to_bf16
+    rng = np.random.default_rng(L * 31 + q + n_h)
+    bf = torch.bfloat16
+    nblk = max(1, (L + BLOCK - 1) // BLOCK)
+    c = round_to_bf16(rng.standard_normal((L, D_C)).astype(np.float32))
+    k = round_to_bf16(rng.standard_normal((L, D_R)).astype(np.float32))
+    qn = round_to_bf16(rng.standard_normal((q, n_h, D_H)).astype(np.float32))
+    qr = round_to_bf16(rng.standard_normal((q, n_h, D_R)).astype(np.float32))
+    wuk = round_to_bf16((rng.standard_normal((n_h, D_H, D_C)) / np.sqrt(D_C)).astype(np.float32))
+    wuv = round_to_bf16((rng.standard_normal((n_h, D_H, D_C)) / np.sqrt(D_C)).astype(np.float32))
+    qpos = np.maximum(np.arange(L - q, L), 0).astype(np.int32)   # rows with no key: any position
+    table = rng.permutation(nblk).astype(np.int32)[None]
+    cache = torch.full((nblk, BLOCK, ROW), float("nan"), dtype=bf, device="cuda")
+    dev = lambda x, dt=bf: torch.from_numpy(np.ascontiguousarray(x)).to(dt).cuda()
+    if L:
+        mla.mla_kv_append(cache, dev(table, torch.int32), dev(c), dev(k),
+                          torch.zeros(L, dtype=torch.int32, device="cuda"),
+                          torch.arange(L, dtype=torch.int32, device="cuda"), ROPE_BASE)
+    out = torch.full((q, n_h, D_H), float("nan"), device="cuda")
+    lse = torch.full((q, n_h), float("nan"), device="cuda")
+    ws = torch.empty(mla.mla_prefill_mha_workspace(L, n_h), dtype=torch.uint8, device="cuda")
+    say(f"prefill_mha L={L} q={q} n_h={n_h}")
+    mla.mla_prefill_mha(dev(qn), dev(qr), dev(qpos, torch.int32), dev(wuk), dev(wuv), cache,
+                        dev(table, torch.int32), np.array([L]), q, softmax_scale(), ROPE_BASE,
+                        out, lse, ws)
+    torch.cuda.synchronize()
+    vis = np.maximum(orc.visible_keys(L, q), 0)
+    ref, lref, _ = orc.mla_attention_naive(c, k, qn, qr, wuk, wuv, np.arange(L), qpos, vis,
+                                           softmax_scale(), ROPE_BASE)
+    got, lgot = to_np(out), to_np(lse)
+    empty = vis == 0
+    assert np.all(got[empty] == 0.0) and np.all(np.isneginf(lgot[empty]))
+    # A row that sees n keys has outputs of order |v| / sqrt(n): rows with few
+    # keys are measured against their own RMS (their bf16 P rounding would
+    # reach ~4e-2 of the chunk-wide RMS), the others against the rows' RMS.
+    short = (vis > 0) & (vis < 16)
+    for m in np.nonzero(short)[0]:
+        assert rel_err(got[m], ref[m]) <= TOL["bf16"], m
+    longer = vis >= 16
+    if longer.any():
+        assert rel_err(got[longer], ref[longer]) <= TOL["bf16"]
+    if (~empty).any():
+        _check_lse(lgot[~empty], lref[~empty])
