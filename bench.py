@@ -106,9 +106,13 @@ def producer_work(T, n_h, d_model, d_cq, esz):
     token); c^Q's round trip through the workspace is not counted.  FLOPs:
     2 per multiply-add of the projections."""
     kv_w = (512 + 64) * d_model
-    q_w = d_cq * d_model + n_h * (128 + 64) * d_cq
+    if d_cq is None:                      # queries straight from h
+        q_w = n_h * (128 + 64) * d_model
+        q_by = (T * d_model + q_w + T * n_h * 192) * esz
+    else:
+        q_w = d_cq * d_model + n_h * (128 + 64) * d_cq
+        q_by = (T * d_model + q_w + T * n_h * 192) * esz + d_cq * 4
     kv_by = (T * d_model + kv_w + T * 576) * esz + 512 * 4
-    q_by = (T * d_model + q_w + T * n_h * 192) * esz + d_cq * 4
     return kv_by, q_by, 2 * T * kv_w, 2 * T * q_w
 
 
@@ -143,8 +147,11 @@ def cpu_baseline(prob, budget_s: float, hid=None):
             c[L - q:], k[L - q:], _ = orc.kv_produce(hid.h[b * q:(b + 1) * q], hid.w_dkv,
                                                      hid.kv_gain, hid.w_kr,
                                                      np.arange(L - q, L), ROPE_BASE, PRODUCER_EPS)
-            _, q_nope, q_rope = orc.q_produce(hid.h[sl], hid.w_dq, hid.q_gain, hid.w_uq,
-                                              hid.w_qr, wl.n_h, PRODUCER_EPS)
+            if hid.w_qc is not None:
+                q_nope, q_rope = orc.q_produce_direct(hid.h[sl], hid.w_qc, hid.w_qr, wl.n_h)
+            else:
+                _, q_nope, q_rope = orc.q_produce(hid.h[sl], hid.w_dq, hid.q_gain, hid.w_uq,
+                                                  hid.w_qr, wl.n_h, PRODUCER_EPS)
         orc.mla_attention_naive(c[:L], k[:L], q_nope, q_rope, prob.w_uk,
                                 prob.w_uv, np.arange(L), prob.q_pos[sl], vis[:rows_per_call],
                                 softmax_scale(), ROPE_BASE)
@@ -177,7 +184,7 @@ def main():
                          "attention (mla_prefill_mha)")
     ap.add_argument("--from-hidden", action="store_true",
                     help="start the step from hidden states: the cache-row and query producers "
-                         "(DeepSeek-V2 widths) replace the append and the given queries")
+                         "(V2 or V2-Lite widths) replace the append and the given queries")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run one plain device-to-device copy of this many bytes (a "
                          "known-size reference for hardware byte counters)")
@@ -192,18 +199,18 @@ def main():
     import torch
     from mla_latent_kv_04_amd import _binding as mla
     from mla_latent_kv_04_amd import pipeline
-    from mla_latent_kv_04_amd.workloads import (D_CQ_V2, D_MODEL_V2, ROPE_BASE, WORKLOADS,
-                                                make_hidden, make_problem, softmax_scale)
+    from mla_latent_kv_04_amd.workloads import (D_CQ_V2, D_MODEL_LITE, D_MODEL_V2, ROPE_BASE,
+                                                WORKLOADS, make_hidden, make_problem,
+                                                softmax_scale)
 
     wl = WORKLOADS[args.workload]
     non_absorbed = args.attention == "non-absorbed"
     if non_absorbed and (wl.q_len == 1 or wl.dtype != "bf16"):
         print("--attention non-absorbed is for bf16 chunked prefill workloads", file=sys.stderr)
         sys.exit(2)
-    if args.from_hidden and wl.n_h != 128:
-        print("--from-hidden uses the DeepSeek-V2 widths (128 heads, query compression); "
-              f"{wl.name} has {wl.n_h} heads", file=sys.stderr)
-        sys.exit(2)
+    # V2 (128 heads): hidden 5120, queries through c^Q (1536); V2-Lite (16
+    # heads): hidden 2048, queries straight from h
+    d_model, d_cq = (D_MODEL_V2, D_CQ_V2) if wl.n_h == 128 else (D_MODEL_LITE, None)
     splits = args.splits if args.splits is not None else wl.num_splits
     log(f"[bench] generating {wl.name} (splits={splits})")
     prob = make_problem(wl)
@@ -215,15 +222,16 @@ def main():
     hid = hw = None
     if args.from_hidden:
         log("[bench] generating hidden states and producer weights")
-        hid = make_hidden(prob)
+        hid = make_hidden(prob, d_model, d_cq)
         hw = {k: (torch.from_numpy(v).cuda() if k.endswith("gain")
                   else pipeline._to_device(v, dp.dtype, "cuda"))
-              for k, v in vars(hid).items()}
+              for k, v in vars(hid).items() if v is not None}
         code = 1 if wl.dtype == "bf16" else 0
-        hw["ws_kv"] = torch.empty(mla.mla_kv_produce_workspace(prob.T, D_MODEL_V2),
+        hw["ws_kv"] = torch.empty(mla.mla_kv_produce_workspace(prob.T, d_model),
                                   dtype=torch.uint8, device="cuda")
-        hw["ws_q"] = torch.empty(mla.mla_q_produce_workspace(prob.T, D_MODEL_V2, D_CQ_V2, code),
-                                 dtype=torch.uint8, device="cuda")
+        if d_cq is not None:
+            hw["ws_q"] = torch.empty(mla.mla_q_produce_workspace(prob.T, d_model, d_cq, code),
+                                     dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
 
     pf_ws = pipeline.prefill_workspace(dp) if non_absorbed else None
@@ -251,8 +259,11 @@ def main():
                                hw["ws_kv"])
             if ev is not None:
                 ev[3].record(stream)
-            mla.mla_q_produce(hw["h"], hw["w_dq"], hw["q_gain"], hw["w_uq"], hw["w_qr"],
-                              dp.q_nope, dp.q_rope, PRODUCER_EPS, hw["ws_q"])
+            if d_cq is not None:
+                mla.mla_q_produce(hw["h"], hw["w_dq"], hw["q_gain"], hw["w_uq"], hw["w_qr"],
+                                  dp.q_nope, dp.q_rope, PRODUCER_EPS, hw["ws_q"])
+            else:
+                mla.mla_q_produce_direct(hw["h"], hw["w_qc"], hw["w_qr"], dp.q_nope, dp.q_rope)
             if ev is not None:
                 ev[4].record(stream)
         mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE)
@@ -330,10 +341,10 @@ def main():
     if hw is not None:
         kv_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
         q_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
-        kv_by, q_by, kv_fl, q_fl = producer_work(prob.T, wl.n_h, D_MODEL_V2, D_CQ_V2,
+        kv_by, q_by, kv_fl, q_fl = producer_work(prob.T, wl.n_h, d_model, d_cq,
                                                  2 if wl.dtype == "bf16" else 4)
         producers = {
-            "d_model": D_MODEL_V2, "d_cq": D_CQ_V2,
+            "d_model": d_model, "d_cq": d_cq,
             "kv_us": round(kv_ms * 1e3, 2), "q_us": round(q_ms * 1e3, 2),
             "kv_algorithmic_bytes": kv_by, "q_algorithmic_bytes": q_by,
             "kv_hbm_frac": round(kv_by / (kv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

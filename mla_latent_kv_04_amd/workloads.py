@@ -39,6 +39,7 @@ BLOCK = 64      # tokens per paged block
 ROPE_BASE = 10000.0
 D_MODEL_V2 = 5120   # DeepSeek-V2 hidden width
 D_CQ_V2 = 1536      # DeepSeek-V2 query compression width d_c'
+D_MODEL_LITE = 2048 # DeepSeek-V2-Lite hidden width (its queries are not compressed)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -218,13 +219,15 @@ class HiddenInputs:
     w_dkv: np.ndarray    # [512, d_model]
     kv_gain: np.ndarray  # [512] float32
     w_kr: np.ndarray     # [64, d_model]
-    w_dq: np.ndarray     # [d_cq, d_model]
-    q_gain: np.ndarray   # [d_cq] float32
-    w_uq: np.ndarray     # [n_h * 128, d_cq]
-    w_qr: np.ndarray     # [n_h * 64, d_cq]
+    w_qr: np.ndarray     # [n_h * 64, d_cq], or [n_h * 64, d_model] without compression
+    w_dq: Optional[np.ndarray] = None    # [d_cq, d_model]   (compressed queries)
+    q_gain: Optional[np.ndarray] = None  # [d_cq] float32
+    w_uq: Optional[np.ndarray] = None    # [n_h * 128, d_cq]
+    w_qc: Optional[np.ndarray] = None    # [n_h * 128, d_model] (uncompressed queries)
 
 
-def make_hidden(prob: Problem, d_model: int = D_MODEL_V2, d_cq: int = D_CQ_V2) -> HiddenInputs:
+def make_hidden(prob: Problem, d_model: int = D_MODEL_V2,
+                d_cq: Optional[int] = D_CQ_V2) -> HiddenInputs:
     """Hidden states for the step's T tokens and random producer weights of the
     DeepSeek-V2 widths (hidden 5120, query compression 1536: adg.csdn.net blog,
     §3.1.1).
@@ -232,12 +235,22 @@ def make_hidden(prob: Problem, d_model: int = D_MODEL_V2, d_cq: int = D_CQ_V2) -
     Recipe (its own ``Generator(PCG64(seed + 7919))``, draws in this order):
     h ~ N(0, 1); W^DKV, W^KR, W^DQ ~ N(0, 1/d_model); W^UQ, W^QR ~ N(0, 1/d_cq);
     the two RMSNorm gains 1 + 0.1 N(0, 1), float32.  Weights are stored
-    [d_out, d_in]; float draws are rounded to bf16 for bf16 workloads."""
+    [d_out, d_in]; float draws are rounded to bf16 for bf16 workloads.
+    d_cq None: queries without compression (V2-Lite: hidden 2048, blog, the
+    V2-Lite paragraph): h; W^DKV, W^KR, W^QC, W^QR ~ N(0, 1/d_model); the
+    latent gain."""
     wl = prob.wl
     bf16 = wl.dtype == "bf16"
     rng = np.random.Generator(np.random.PCG64(wl.seed + 7919))
     T, n_h = prob.T, wl.n_h
     h = _normal(rng, (T, d_model), 1.0, bf16)
+    if d_cq is None:
+        w_dkv = _normal(rng, (D_C, d_model), 1.0 / math.sqrt(d_model), bf16)
+        w_kr = _normal(rng, (D_R, d_model), 1.0 / math.sqrt(d_model), bf16)
+        w_qc = _normal(rng, (n_h * D_H, d_model), 1.0 / math.sqrt(d_model), bf16)
+        w_qr = _normal(rng, (n_h * D_R, d_model), 1.0 / math.sqrt(d_model), bf16)
+        kv_gain = (1.0 + 0.1 * rng.standard_normal(D_C)).astype(np.float32)
+        return HiddenInputs(h=h, w_dkv=w_dkv, kv_gain=kv_gain, w_kr=w_kr, w_qr=w_qr, w_qc=w_qc)
     w_dkv = _normal(rng, (D_C, d_model), 1.0 / math.sqrt(d_model), bf16)
     w_kr = _normal(rng, (D_R, d_model), 1.0 / math.sqrt(d_model), bf16)
     w_dq = _normal(rng, (d_cq, d_model), 1.0 / math.sqrt(d_model), bf16)
