@@ -258,6 +258,9 @@ void proj_bf16(XSrc X, int T, int K, int kc, ProjOut p0, ProjOut p1, hipStream_t
   if (tt == 64)
     hipLaunchKernelGGL((proj_bf16_kernel<OUTM, 64, 3, 64>), grid, block, 0, stream, X, T, K, kc,
                        p0, p1, tiles0);
+  else if (tt == 256)
+    hipLaunchKernelGGL((proj_bf16_kernel<OUTM, 256, 3, 64>), grid, block, 0, stream, X, T, K, kc,
+                       p0, p1, tiles0);
   else
     hipLaunchKernelGGL((proj_bf16_kernel<OUTM, 128, 4, 64>), grid, block, 0, stream, X, T, K, kc,
                        p0, p1, tiles0);

@@ -156,9 +156,9 @@ def test_producers_reject_bad_arguments_and_size_their_workspace(lib):
 def test_prefill_mha_rejects_bad_arguments_and_sizes_its_workspace(lib):
     import numpy as np
     ws = lib.mla_prefill_mha_workspace
-    # k^C and v^C (hi + lo) of the longest sequence, rows padded to a multiple of 128
+    # k^C and v^C (hi + lo) of the longest sequence, rows padded to a multiple of 256
     assert ws(8192, 128) == 3 * 128 * 128 * 8192 * 2
-    assert ws(1, 16) == ws(128, 16) == 3 * 16 * 128 * 128 * 2
+    assert ws(1, 16) == ws(256, 16) == 3 * 16 * 128 * 256 * 2
     assert ws(-1, 16) == -1 and ws(10, 0) == -1
     lens = np.array([300, 200], dtype=np.int32)
     need = ws(300, 16)
