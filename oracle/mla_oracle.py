@@ -51,7 +51,7 @@ __all__ = [
     "rope_rotate", "mla_attention_naive", "kv_cache_rows", "absorb_query",
     "latent_attention", "split_ranges", "combine_splits", "out_projection",
     "visible_keys", "mla_reference_problem", "rms_norm", "kv_produce", "q_produce",
-    "q_produce_direct",
+    "q_produce_direct", "o_projection",
 ]
 
 F64 = np.float64
@@ -332,4 +332,13 @@ def q_produce_direct(h, w_qc, w_qr, n_h: int):
     q_nope = (h @ np.asarray(w_qc, F64).T).reshape(T, n_h, -1)
     q_rope = (h @ np.asarray(w_qr, F64).T).reshape(T, n_h, -1)
     return q_nope, q_rope
+
+
+def o_projection(out, w_o):
+    """The layer output of eq. 8 (notes §2.1.1): u_t = W^O [o_{t,1}; ...; o_{t,n_h}],
+    the heads' outputs out [T, n_h, d_h] concatenated head after head, and
+    W^O [d_model, n_h * d_h] stored [d_out, d_in].  Returns u [T, d_model]."""
+    out = np.asarray(out, F64)
+    T = out.shape[0]
+    return out.reshape(T, -1) @ np.asarray(w_o, F64).T
 

@@ -415,3 +415,21 @@ def test_direct_query_producer_matches_scalar_loops():
                                 n_h, eps)
     np.testing.assert_allclose(qn2, qn, rtol=1e-9, atol=1e-9)
     np.testing.assert_allclose(qr2, qr, rtol=1e-9, atol=1e-9)
+
+
+def test_o_projection_matches_scalar_loops():
+    """eq. 8's u = W^O [o_1; ...; o_nh] against element-by-element sums (a
+    head order or a transposed W^O fails), and a W^O that picks one head's
+    dimension returns that output."""
+    rng = np.random.default_rng(5)
+    T, n_h, d_h, d_model = 3, 2, 4, 5
+    out = rng.standard_normal((T, n_h, d_h))
+    w_o = rng.standard_normal((d_model, n_h * d_h))
+    u = orc.o_projection(out, w_o)
+    for t in range(T):
+        for i in range(d_model):
+            want = sum(w_o[i][h * d_h + d] * out[t][h][d] for h in range(n_h) for d in range(d_h))
+            assert abs(u[t][i] - want) < 1e-12
+    pick = np.zeros((1, n_h * d_h))
+    pick[0, 1 * d_h + 2] = 1.0                 # head 1, dimension 2
+    np.testing.assert_array_equal(orc.o_projection(out, pick)[:, 0], out[:, 1, 2])
