@@ -152,9 +152,11 @@ def cpu_baseline(prob, budget_s: float, hid=None):
             else:
                 _, q_nope, q_rope = orc.q_produce(hid.h[sl], hid.w_dq, hid.q_gain, hid.w_uq,
                                                   hid.w_qr, wl.n_h, PRODUCER_EPS)
-        orc.mla_attention_naive(c[:L], k[:L], q_nope, q_rope, prob.w_uk,
-                                prob.w_uv, np.arange(L), prob.q_pos[sl], vis[:rows_per_call],
-                                softmax_scale(), ROPE_BASE)
+        o, _, _ = orc.mla_attention_naive(c[:L], k[:L], q_nope, q_rope, prob.w_uk, prob.w_uv,
+                                          np.arange(L), prob.q_pos[sl], vis[:rows_per_call],
+                                          softmax_scale(), ROPE_BASE)
+        if hid is not None and hid.w_o is not None:
+            orc.o_projection(o, hid.w_o)                  # eq. 8, as the step ends
         done_rows += rows_per_call
         done_seqs += 1
         keys += L
@@ -232,6 +234,9 @@ def main():
         if d_cq is not None:
             hw["ws_q"] = torch.empty(mla.mla_q_produce_workspace(prob.T, d_model, d_cq, code),
                                      dtype=torch.uint8, device="cuda")
+        hw["ws_o"] = torch.empty(max(1, mla.mla_o_proj_workspace(prob.T, wl.n_h, d_model, code)),
+                                 dtype=torch.uint8, device="cuda")
+        hw["u"] = torch.empty((prob.T, d_model), dtype=dp.dtype, device="cuda")
         torch.cuda.synchronize()
 
     pf_ws = pipeline.prefill_workspace(dp) if non_absorbed else None
@@ -285,6 +290,12 @@ def main():
             # the split rows' merge runs inside the projection's loads
             mla.mla_out_proj_planned(dp.o_lat, dp.o_part, dp.lse_part, dp.split, dp.w_uv,
                                      dp.out, dp.lse)
+            if hw is not None:             # eq. 8: the layer's output u = W^O [o_1; ...]
+                if ev is not None:
+                    ev[5].record(stream)
+                mla.mla_o_proj(dp.out, hw["w_o"], hw["u"], hw["ws_o"])
+                if ev is not None:
+                    ev[6].record(stream)
             return
         if splits > 1:
             mla.mla_splitkv_combine(dp.o_part, dp.lse_part, dp.B, splits, dp.q_len, dp.n_h,
@@ -305,7 +316,7 @@ def main():
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    n_ev = 5 if hw is not None else 2
+    n_ev = 7 if hw is not None else 2
     events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(n_ev))
               for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
@@ -341,6 +352,10 @@ def main():
     if hw is not None:
         kv_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
         q_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
+        o_ms = (float(np.mean([e[5].elapsed_time(e[6]) for e in events]))
+                if splits == 0 else None)
+        o_by = (prob.T * wl.n_h * 128 * 4 + d_model * wl.n_h * 128 * (2 if wl.dtype == "bf16" else 4)
+                + prob.T * d_model * (2 if wl.dtype == "bf16" else 4))
         kv_by, q_by, kv_fl, q_fl = producer_work(prob.T, wl.n_h, d_model, d_cq,
                                                  2 if wl.dtype == "bf16" else 4)
         producers = {
@@ -351,8 +366,13 @@ def main():
             "q_hbm_frac": round(q_by / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "kv_mfma_frac": round(kv_fl / (kv_ms * 1e-3) / 1e12 / mfma_peak, 4),
             "q_mfma_frac": round(q_fl / (q_ms * 1e-3) / 1e12 / mfma_peak, 4),
+            "o_proj_us": None if o_ms is None else round(o_ms * 1e3, 2),
+            "o_proj_algorithmic_bytes": o_by,
+            "o_proj_hbm_frac": (None if o_ms is None else
+                                round(o_by / (o_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)),
         }
-        log(f"[bench] producers: kv {kv_ms * 1e3:.1f} us, q {q_ms * 1e3:.1f} us")
+        log(f"[bench] producers: kv {kv_ms * 1e3:.1f} us, q {q_ms * 1e3:.1f} us"
+            + ("" if o_ms is None else f"; W^O {o_ms * 1e3:.1f} us"))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -366,7 +386,8 @@ def main():
            "work_items": (int(dp.work.shape[0]) if splits == 0 else dp.B * dp.q_len * splits),
            "d_c": 512, "d_R": 64, "d_h": 128,
            "attention_form": args.attention,
-           "step_input": ("hidden states (cache-row and query producers in the step)"
+           "step_input": ("hidden states (cache-row and query producers in the step; the "
+                          "step ends with eq. 8's W^O when the plan is balanced)"
                           if hw is not None else "new latent rows and per-head queries")}
     rec = {
         "metric": "MLA decode tokens/s (+ attention-kernel HBM GB/s and MFMA share of peak), "

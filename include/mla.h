@@ -348,6 +348,21 @@ int32_t mla_q_produce_direct(const void* h, const void* w_qc, const void* w_qr, 
                              void* q_rope, void* stream);
 
 /*
+ * mla_o_proj - the layer output of eq. 8 (notes §2.1.1):
+ *   u[t] = W^O [o_{t,1}; ...; o_{t,n_h}]
+ * out: fp32 [T, n_h, 128] as mla_out_proj writes it; w_o [d_model, n_h * 128]
+ * in dtype; u [T, d_model] in dtype.  In bf16 the heads' outputs are rounded
+ * to bf16 once to feed the MFMA (fp32 accumulation).  The caller's workspace
+ * holds that copy and split-K partials: at least mla_o_proj_workspace bytes
+ * (-1 there: invalid sizes; 0 is possible, then workspace may be NULL).
+ * d_model a multiple of 64.
+ */
+int64_t mla_o_proj_workspace(int32_t T, int32_t n_h, int32_t d_model, int32_t dtype);
+int32_t mla_o_proj(const float* out, const void* w_o, int32_t T, int32_t n_h, int32_t d_model,
+                   int32_t dtype, void* u, void* workspace, int64_t workspace_bytes,
+                   void* stream);
+
+/*
  * Non-absorbed chunked prefill: the literal form of eq. 7 (notes §2.1.1) with
  * the per-head keys and values of eq. 10-11 (notes §2.1.2),
  *   k^C_{j,i} = W^UK_i c^KV_j,  v^C_{j,i} = W^UV_i c^KV_j,

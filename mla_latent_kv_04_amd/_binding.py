@@ -23,6 +23,7 @@ _EXPORTS = ("mla_status_string", "mla_abi_version", "mla_kv_append", "mla_absorb
             "mla_plan_decode", "mla_decode_paged_planned", "mla_combine_planned",
             "mla_out_proj_planned", "mla_kv_produce_workspace", "mla_kv_produce",
             "mla_q_produce_workspace", "mla_q_produce", "mla_q_produce_direct",
+            "mla_o_proj_workspace", "mla_o_proj",
             "mla_prefill_mha_workspace", "mla_prefill_mha")
 
 
@@ -74,6 +75,8 @@ def load() -> ctypes.CDLL:
         "mla_q_produce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P,
                                ctypes.c_int64, _P]),
         "mla_q_produce_direct": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+        "mla_o_proj_workspace": (ctypes.c_int64, [_I, _I, _I, _I]),
+        "mla_o_proj": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_int64, _P]),
         "mla_prefill_mha_workspace": (ctypes.c_int64, [_I, _I]),
         "mla_prefill_mha": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F,
                                  _F, _P, _P, _P, ctypes.c_int64, _P]),
@@ -482,3 +485,31 @@ def mla_q_produce_direct(h, w_qc, w_qr, q_nope, q_rope, stream=None):
                                      d_model, n_h, dt, _dev(q_nope, "q_nope"),
                                      _dev(q_rope, "q_rope"), _stream(stream))
     _check("mla_q_produce_direct", st)
+
+
+def mla_o_proj_workspace(T, n_h, d_model, dtype_code):
+    """Workspace bytes of mla_o_proj (see mla.h)."""
+    n = int(load().mla_o_proj_workspace(int(T), int(n_h), int(d_model), int(dtype_code)))
+    if n < 0:
+        raise ValueError("invalid sizes for mla_o_proj_workspace")
+    return n
+
+
+def mla_o_proj(out, w_o, u, workspace=None, stream=None):
+    """eq. 8's u = W^O [o_1; ...; o_nh] (see mla.h).  out fp32 [T, n_h, 128]."""
+    torch = _torch()
+    dt = _dtype_code(w_o)
+    T, n_h = int(out.shape[0]), int(out.shape[1])
+    d_model = int(w_o.shape[0])
+    if tuple(out.shape) != (T, n_h, D_H) or out.dtype != torch.float32:
+        raise ValueError("out must be fp32 [T, n_h, 128]")
+    if tuple(w_o.shape) != (d_model, n_h * D_H) or tuple(u.shape) != (T, d_model):
+        raise ValueError("w_o must be [d_model, n_h*128] and u [T, d_model]")
+    if u.dtype != w_o.dtype:
+        raise TypeError("u must have w_o's dtype")
+    if workspace is not None and workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    st = load().mla_o_proj(_dev(out, "out", torch.float32), _dev(w_o, "w_o"), T, n_h, d_model, dt,
+                           _dev(u, "u"), _dev(workspace, "workspace"),
+                           0 if workspace is None else int(workspace.numel()), _stream(stream))
+    _check("mla_o_proj", st)

@@ -67,6 +67,11 @@ hipError_t launch_q_produce_direct(const void* h, const void* w_qc, const void* 
                                    int d_model, int n_h, int dtype, void* q_nope, void* q_rope,
                                    hipStream_t stream);
 
+// eq. 8's output projection (produce.hip).
+long o_proj_workspace(int T, int n_h, int d_model, int dtype);
+hipError_t launch_o_proj(const float* out, const void* w_o, int T, int n_h, int d_model,
+                         int dtype, void* u, void* workspace, hipStream_t stream);
+
 // Non-absorbed chunked prefill (prefill_mha.hip), bf16.  seq_lens is a host
 // array; the workspace holds k^C and v^C^T of the longest sequence.
 long prefill_mha_workspace(int max_len, int n_h);

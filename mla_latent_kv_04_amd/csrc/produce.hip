@@ -348,7 +348,102 @@ hipError_t q_direct(const void* h, const void* w_qc, const void* w_qr, int T, in
   return hipGetLastError();
 }
 
+// fp32 [n] -> bf16, eight elements per thread and pass (n a multiple of 8).
+__global__ void __launch_bounds__(256) to_bf16_kernel(const float* __restrict__ x, long n,
+                                                      uint16_t* __restrict__ y) {
+  for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (long)gridDim.x * 256 * 8) {
+    const float4 a = *reinterpret_cast<const float4*>(x + i);
+    const float4 b = *reinterpret_cast<const float4*>(x + i + 4);
+    *reinterpret_cast<uint4*>(y + i) = uint4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
+                                             pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
+  }
+}
+
+// y[i] = sum over z < S of part[z n + i], in the element type (n a multiple of 4).
+template <class E>
+__global__ void __launch_bounds__(256) sum_parts_kernel(const float* __restrict__ part, int S,
+                                                        long n, typename E::storage* __restrict__ y) {
+  for (long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (long)gridDim.x * 256 * 4) {
+    float4 v = *reinterpret_cast<const float4*>(part + i);
+    for (int z = 1; z < S; ++z) {
+      const float4 w = *reinterpret_cast<const float4*>(part + (long)z * n + i);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    y[i] = E::from_f32(v.x);
+    y[i + 1] = E::from_f32(v.y);
+    y[i + 2] = E::from_f32(v.z);
+    y[i + 3] = E::from_f32(v.w);
+  }
+}
+
+// K slice length of W^O: its weights (d_model x n_h 128) dwarf the fp32
+// partials of a decode batch, so slice for about 1024 workgroups while the
+// partials stay within 1/8 of the weight bytes (S <= K / (16 T)), each slice
+// at least 512 long and a multiple of 64.
+int o_chunk(int T, int N, int K) {
+  const int tt = t_tile(T, N);
+  const long tiles = (long)((N + PN - 1) / PN) * ((T + tt - 1) / tt);
+  const long cap = std::max(1L, std::min((long)K / 512, (long)K / (16L * std::max(T, 1))));
+  const int S = (int)std::max(1L, std::min((1024 + tiles - 1) / tiles, cap));
+  return ((K + S - 1) / S + PK - 1) / PK * PK;
+}
+
+// eq. 8: u = W^O [o_1; ...; o_nh] for T rows of the heads' fp32 outputs.  In
+// bf16 the outputs are rounded to bf16 once (workspace) to feed the MFMA;
+// K = n_h 128 is split over workgroups into fp32 partials when the output
+// tiles alone would leave the chip idle.
+template <class E>
+hipError_t o_proj(const float* out, const void* w_o, int T, int n_h, int d_model, void* u,
+                  void* workspace, hipStream_t stream) {
+  const int K = n_h * D_H;
+  const int kc = o_chunk(T, d_model, K);
+  const int S = (K + kc - 1) / kc;
+  char* ws = static_cast<char*>(workspace);
+  const long xb = E::bytes == 2 ? ((long)T * K * 2 + 255) / 256 * 256 : 0;
+  float* part = reinterpret_cast<float*>(ws + xb);
+  const long n = (long)T * d_model;
+  const int grid = (int)std::min<long>(4096, (n + 1023) / 1024);
+  if constexpr (E::bytes == 2) {
+    auto* xh = reinterpret_cast<uint16_t*>(ws);
+    const long nx = (long)T * K;
+    hipLaunchKernelGGL(to_bf16_kernel, dim3((int)std::min<long>(4096, (nx + 2047) / 2048)),
+                       dim3(256), 0, stream, out, nx, xh);
+    if (S == 1) {
+      proj_bf16<OUT_ROWS>(XSrc{xh, K, nullptr, 0}, T, K, K,
+                          ProjOut{static_cast<const uint16_t*>(w_o), d_model, u, d_model, 0, 0},
+                          ProjOut{nullptr, 0, nullptr, 0, 0, 0}, stream);
+      return hipGetLastError();
+    }
+    proj_bf16<OUT_PARTIAL>(XSrc{xh, K, nullptr, 0}, T, K, kc,
+                           ProjOut{static_cast<const uint16_t*>(w_o), d_model, part, d_model, 0, 0},
+                           ProjOut{nullptr, 0, nullptr, 0, 0, 0}, stream);
+  } else {
+    if (S == 1) {
+      gemm_f32<E>(out, w_o, T, d_model, K, K, true, nullptr, d_model, 0, u, stream);
+      return hipGetLastError();
+    }
+    gemm_f32<E>(out, w_o, T, d_model, K, kc, false, part, d_model, 0, nullptr, stream);
+  }
+  hipLaunchKernelGGL(sum_parts_kernel<E>, dim3(grid), dim3(256), 0, stream, part, S, n,
+                     static_cast<typename E::storage*>(u));
+  return hipGetLastError();
+}
+
 }  // namespace
+
+long o_proj_workspace(int T, int n_h, int d_model, int dtype) {
+  const int K = n_h * D_H;
+  const long xb = dtype == 1 ? ((long)T * K * 2 + 255) / 256 * 256 : 0;
+  const int kc = o_chunk(T, d_model, K);
+  const int S = (K + kc - 1) / kc;
+  return xb + (S > 1 ? (long)S * T * d_model * 4 : 0);
+}
+
+hipError_t launch_o_proj(const float* out, const void* w_o, int T, int n_h, int d_model,
+                         int dtype, void* u, void* workspace, hipStream_t stream) {
+  if (dtype == 1) return o_proj<BF16>(out, w_o, T, n_h, d_model, u, workspace, stream);
+  return o_proj<F32>(out, w_o, T, n_h, d_model, u, workspace, stream);
+}
 
 hipError_t launch_q_produce_direct(const void* h, const void* w_qc, const void* w_qr, int T,
                                    int d_model, int n_h, int dtype, void* q_nope, void* q_rope,

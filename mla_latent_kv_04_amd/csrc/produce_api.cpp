@@ -100,6 +100,30 @@ int32_t mla_q_produce_direct(const void* h, const void* w_qc, const void* w_qr, 
                                                  q_rope, (hipStream_t)stream));
 }
 
+int64_t mla_o_proj_workspace(int32_t T, int32_t n_h, int32_t d_model, int32_t dtype) {
+  if (T < 0 || n_h < 1 || n_h > 1024 || d_model < 64 || d_model % 64 != 0 || !dtype_ok(dtype))
+    return -1;
+  return mla::o_proj_workspace(T, n_h, d_model, dtype);
+}
+
+int32_t mla_o_proj(const float* out, const void* w_o, int32_t T, int32_t n_h, int32_t d_model,
+                   int32_t dtype, void* u, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+  if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  if (T < 0 || n_h < 1 || n_h > 1024 || d_model < 64 || d_model % 64 != 0) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!fits_2g(T, (int64_t)n_h * 128) || !fits_2g(d_model, (int64_t)n_h * 128) ||
+      !fits_2g(T, d_model))
+    return MLA_ERR_SHAPE;
+  const int64_t need = mla::o_proj_workspace(T, n_h, d_model, dtype);
+  if (workspace_bytes < need) return MLA_ERR_SHAPE;
+  if (!out || !w_o || !u || (need > 0 && !workspace)) return MLA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(w_o) || !aligned16(u) || (need > 0 && !aligned16(workspace)))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_o_proj(out, w_o, T, n_h, d_model, dtype, u, workspace,
+                                       (hipStream_t)stream));
+}
+
 int64_t mla_prefill_mha_workspace(int32_t max_seq_len, int32_t n_h) {
   if (max_seq_len < 0 || n_h < 1 || n_h > 1024) return -1;
   return mla::prefill_mha_workspace(max_seq_len, n_h);

@@ -224,6 +224,7 @@ class HiddenInputs:
     q_gain: Optional[np.ndarray] = None  # [d_cq] float32
     w_uq: Optional[np.ndarray] = None    # [n_h * 128, d_cq]
     w_qc: Optional[np.ndarray] = None    # [n_h * 128, d_model] (uncompressed queries)
+    w_o: Optional[np.ndarray] = None     # [d_model, n_h * 128] (eq. 8's output projection)
 
 
 def make_hidden(prob: Problem, d_model: int = D_MODEL_V2,
@@ -238,7 +239,7 @@ def make_hidden(prob: Problem, d_model: int = D_MODEL_V2,
     [d_out, d_in]; float draws are rounded to bf16 for bf16 workloads.
     d_cq None: queries without compression (V2-Lite: hidden 2048, blog, the
     V2-Lite paragraph): h; W^DKV, W^KR, W^QC, W^QR ~ N(0, 1/d_model); the
-    latent gain."""
+    latent gain.  Last in either case: W^O ~ N(0, 1/(n_h 128))."""
     wl = prob.wl
     bf16 = wl.dtype == "bf16"
     rng = np.random.Generator(np.random.PCG64(wl.seed + 7919))
@@ -250,7 +251,9 @@ def make_hidden(prob: Problem, d_model: int = D_MODEL_V2,
         w_qc = _normal(rng, (n_h * D_H, d_model), 1.0 / math.sqrt(d_model), bf16)
         w_qr = _normal(rng, (n_h * D_R, d_model), 1.0 / math.sqrt(d_model), bf16)
         kv_gain = (1.0 + 0.1 * rng.standard_normal(D_C)).astype(np.float32)
-        return HiddenInputs(h=h, w_dkv=w_dkv, kv_gain=kv_gain, w_kr=w_kr, w_qr=w_qr, w_qc=w_qc)
+        w_o = _normal(rng, (d_model, n_h * D_H), 1.0 / math.sqrt(n_h * D_H), bf16)
+        return HiddenInputs(h=h, w_dkv=w_dkv, kv_gain=kv_gain, w_kr=w_kr, w_qr=w_qr, w_qc=w_qc,
+                            w_o=w_o)
     w_dkv = _normal(rng, (D_C, d_model), 1.0 / math.sqrt(d_model), bf16)
     w_kr = _normal(rng, (D_R, d_model), 1.0 / math.sqrt(d_model), bf16)
     w_dq = _normal(rng, (d_cq, d_model), 1.0 / math.sqrt(d_model), bf16)
@@ -258,6 +261,7 @@ def make_hidden(prob: Problem, d_model: int = D_MODEL_V2,
     w_qr = _normal(rng, (n_h * D_R, d_cq), 1.0 / math.sqrt(d_cq), bf16)
     kv_gain = (1.0 + 0.1 * rng.standard_normal(D_C)).astype(np.float32)
     q_gain = (1.0 + 0.1 * rng.standard_normal(d_cq)).astype(np.float32)
+    w_o = _normal(rng, (d_model, n_h * D_H), 1.0 / math.sqrt(n_h * D_H), bf16)
     return HiddenInputs(h=h, w_dkv=w_dkv, kv_gain=kv_gain, w_kr=w_kr, w_dq=w_dq, q_gain=q_gain,
-                        w_uq=w_uq, w_qr=w_qr)
+                        w_uq=w_uq, w_qr=w_qr, w_o=w_o)
 

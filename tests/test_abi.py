@@ -193,3 +193,21 @@ def test_direct_query_producer_rejects_bad_arguments(lib):
     assert q(wr=NULL) == 1 and q(qn=NULL) == 1
     assert q(qr=MISALIGNED) == 3
     assert q(T=0, h=NULL) == 0
+
+
+def test_o_proj_rejects_bad_arguments_and_sizes_its_workspace(lib):
+    ws = lib.mla_o_proj_workspace
+    assert ws(128, 128, 5120, 1) >= 128 * 128 * 128 * 2        # the bf16 copy of the outputs
+    assert ws(128, 128, 5120, 7) == -1 and ws(128, 0, 5120, 1) == -1 and ws(128, 128, 100, 1) == -1
+    need = ws(4, 2, 64, 1)
+
+    def o(**kw):
+        a = dict(out=FAKE, w=FAKE, T=4, nh=2, dm=64, dt=1, u=FAKE, ws=FAKE, wb=need)
+        a.update(kw)
+        return lib.mla_o_proj(a["out"], a["w"], a["T"], a["nh"], a["dm"], a["dt"], a["u"], a["ws"],
+                              a["wb"], None)
+    assert o(dt=3) == 4
+    assert o(dm=96) == 2 and o(nh=0) == 2 and o(wb=need - 1) == 2
+    assert o(w=NULL) == 1 and o(u=NULL) == 1
+    assert o(out=MISALIGNED) == 3
+    assert o(T=0, out=NULL) == 0

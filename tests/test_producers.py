@@ -151,6 +151,37 @@ def test_direct_query_producer_matches_oracle(dtype, d_model, n_h):
             assert rel_err(g, ref) <= 1e-5
 
 
+@pytest.mark.parametrize("dtype,T,n_h,d_model", [("bf16", 128, 128, 5120), ("f32", 33, 2, 192)])
+def test_o_proj_matches_oracle(dtype, T, n_h, d_model):
+    """eq. 8's u = W^O [o_1; ...; o_nh]: at the V2 shape (128 tokens, 128 heads,
+    hidden 5120: K split over workgroups) and a small fp32 case."""
+    import torch
+    from mla_latent_kv_04_amd import _binding as mla
+    rng = np.random.default_rng(T + n_h)
+    out = rng.standard_normal((T, n_h, D_H)).astype(np.float32)
+    w_o = _weights(rng, (d_model, n_h * D_H), n_h * D_H, dtype)
+    ref = orc.o_projection(out, w_o)
+    say(f"o_proj {dtype} T={T} n_h={n_h} d_model={d_model}")
+    code = 1 if dtype == "bf16" else 0
+    u = torch.empty((T, d_model), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                    device="cuda")
+    n = mla.mla_o_proj_workspace(T, n_h, d_model, code)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    mla.mla_o_proj(torch.from_numpy(out).cuda(), _dev(w_o, dtype), u, ws)
+    torch.cuda.synchronize()
+    got = u.float().cpu().numpy().astype(np.float64)
+    assert ref.size <= 1 << 20
+    if dtype == "bf16":
+        # out rounded to bf16 once, fp32 accumulation, u rounded to bf16
+        assert rel_err(got, ref) <= TOL["bf16"]
+        cast = round_to_bf16(out).astype(np.float64)
+        want = orc.o_projection(cast, w_o)
+        rms = np.sqrt(np.mean(want ** 2))
+        assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + rms * 1e-4)
+    else:
+        assert rel_err(got, ref) <= 1e-5
+
+
 def test_hidden_states_to_attention_output():
     """Cache rows and the query produced from hidden states, then absorb,
     attention and out-projection, against the oracle's producers followed by
