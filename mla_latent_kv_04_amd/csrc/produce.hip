@@ -1,4 +1,5 @@
-// Cache and query producers: the projections that feed the attention path.
+// Cache and query producers, the projections that feed the attention path,
+// and eq. 8's output projection W^O, which ends an attention layer.
 //
 //   c^KV = RMSNorm(W^DKV h), k^R = W^KR h          (eq. 9 of the DeepSeek-V2
 //   c^Q  = RMSNorm(W^DQ h),  q^C = W^UQ c^Q,        notes, irregular6612.github.io,
@@ -17,7 +18,10 @@
 // Narrow projections (576 or d_cq outputs) split K over workgroups to fill
 // the chip and write fp32 partial sums; one workgroup per token adds them up
 // before the RMSNorm (and, for the cache row, the key rotation and the paged
-// write).  fp32 takes a plain MFMA kernel without LDS.
+// write).  A model without query compression (V2-Lite) takes both query parts
+// straight from h in one launch.  W^O rounds the heads' fp32 outputs to bf16
+// once, splits its long K over workgroups and sums the partials.  fp32 takes
+// a plain MFMA kernel without LDS.
 #include <algorithm>
 
 #include "mla_common.h"
