@@ -123,11 +123,12 @@ def cpu_baseline(prob, budget_s: float, hid=None):
     import numpy as np
     from oracle import mla_oracle as orc
     from mla_latent_kv_04_amd.workloads import ROPE_BASE, softmax_scale
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        threads = None
     wl = prob.wl
     q = wl.q_len
     done_rows = 0
@@ -165,8 +166,18 @@ def cpu_baseline(prob, budget_s: float, hid=None):
     dt = time.perf_counter() - t0
     sample = (f"{done_seqs} of {wl.B} sequences, {done_rows} query rows x {wl.n_h} heads, "
               f"{keys} cached keys; non-absorbed float64 NumPy oracle")
-    return {"value": done_rows / dt, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 2)}
+    return {"value": done_rows / dt, "unit": "tokens/s", "cores": cores,
+            "blas_threads": threads, "kind": "oracle", "sample": sample,
+            "seconds": round(dt, 2)}
+
+
+def spread(xs):
+    """Mean, median, 10th and 90th percentile of a list of times (ms -> us)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64) * 1e3
+    return {"mean": round(float(a.mean()), 2), "median": round(float(np.median(a)), 2),
+            "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
 
 
 def main():
@@ -176,6 +187,13 @@ def main():
     # caches; the timed region is then steady state
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=300)
+    # after the requested warm-up, untimed steps continue until this much wall
+    # time has passed: a fresh device raises its clocks over the first tens of
+    # milliseconds of load, and a short warm-up would time that ramp
+    ap.add_argument("--settle-seconds", type=float, default=0.5)
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra steps, each after a 1 GiB write that evicts the caches, "
+                         "timed separately (reported as cold; 0 = skip)")
     ap.add_argument("--workload", default="v2_bf16_B128_L1k-8k")
     ap.add_argument("--splits", type=int, default=None,
                     help="split-KV partitions per row; 0 = balanced work plan (default: workload's)")
@@ -313,21 +331,48 @@ def main():
         del src, dst
 
     log(f"[bench] warmup {args.warmup}")
+    tw = time.perf_counter()
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
+    settle = 0
+    while time.perf_counter() - tw < args.settle_seconds:
+        for _ in range(20):
+            one_step()
+        settle += 20
+        torch.cuda.synchronize()
     n_ev = 7 if hw is not None else 2
     events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(n_ev))
               for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
+    step_ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+               for _ in range(args.steps)]
+    log(f"[bench] {settle} settle steps; timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        step_ev[i][0].record(stream)
         one_step(events[i])
+        step_ev[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    dec_times = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = float(np.mean(dec_times))
+    timing = {"attention_us": spread(dec_times),
+              "step_us": spread([e[0].elapsed_time(e[1]) for e in step_ev]),
+              "warmup_steps": args.warmup, "settle_steps": settle}
+    if args.cold_steps > 0:
+        # each step after a 1 GiB write: the cache rows, queries and weights
+        # come from HBM, not from the L2 / last-level cache
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        cold = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(n_ev))
+                for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            flush.fill_(float(i))
+            one_step(cold[i])
+        torch.cuda.synchronize()
+        timing["attention_cold_us"] = spread([e[0].elapsed_time(e[1]) for e in cold])
+        del flush
     tokens = prob.T
     value = tokens / (ms_per_step * 1e-3)
 
@@ -395,7 +440,7 @@ def main():
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": cfg, "roofline": roof,
+        "config": cfg, "roofline": roof, "timing": timing,
         "attention_kernel": {"scope": ("mla_prefill_mha: k^C and v^C projections, then the "
                                        "attention kernel" if non_absorbed else
                                        "the paged attention kernel"),

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+#define MLA_ABI_VERSION 2
 
 #define MLA_D_C 512
 #define MLA_D_R 64
@@ -248,6 +248,10 @@ int32_t mla_plan_decode(const int32_t* seq_lens, int32_t B, int32_t q_len, int32
  * row's query against keys [key_begin, key_end) of the row's sequence
  * (b = row / q_len) and writes o_lat/lse row `row` when slot < 0, else
  * o_part/lse_part row `slot` (fp32 [n_parts, n_h, 512] / [n_parts, n_h]).
+ * n_parts >= 0 is the number of partial rows the caller provides (o_part and
+ * lse_part may be NULL only when it is 0); an item whose slot is >= n_parts,
+ * or whose row is outside [0, B * q_len), is skipped on the device and
+ * writes nothing.
  * lists (device int32 [n_lists + 1], may be NULL): the items of each list are
  * run in order by one workgroup per 64 heads; results do not depend on it
  * (NULL runs one item per workgroup).  Other arguments as in
@@ -258,8 +262,8 @@ int32_t mla_decode_paged_planned(const void* q_lat, const void* kv_cache, int32_
                                  int32_t max_blocks, int32_t B, int32_t q_len, int32_t n_h,
                                  int32_t dtype, float softmax_scale, const int32_t* work,
                                  int32_t n_work, const int32_t* lists, int32_t n_lists,
-                                 float* o_part, float* lse_part, float* o_lat, float* lse,
-                                 void* stream);
+                                 float* o_part, float* lse_part, int32_t n_parts, float* o_lat,
+                                 float* lse, void* stream);
 
 /*
  * mla_combine_planned - merge the partials of every split row of a plan

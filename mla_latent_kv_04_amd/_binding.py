@@ -65,7 +65,7 @@ def load() -> ctypes.CDLL:
         "mla_split_plan": (_I, [_P, _I, _I, _I, _P]),
         "mla_plan_decode": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
         "mla_decode_paged_planned": (_I, [_P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _F, _P, _I,
-                                          _P, _I, _P, _P, _P, _P, _P]),
+                                          _P, _I, _P, _P, _I, _P, _P, _P]),
         "mla_combine_planned": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
         "mla_out_proj_planned": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
         "mla_kv_produce_workspace": (ctypes.c_int64, [_I, _I]),
@@ -318,8 +318,8 @@ def mla_decode_paged_planned(q_lat, kv_cache, block_table, B, q_len, softmax_sca
         int(block_table.shape[1]), int(B), int(q_len), n_h, dt, float(softmax_scale),
         _dev(work, "work", torch.int32), int(work.shape[0]), _dev(lists, "lists", torch.int32),
         int(lists.shape[0]) - 1 if lists is not None else 0, _dev(o_part, "o_part", f32),
-        _dev(lse_part, "lse_part", f32), _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32),
-        _stream(stream))
+        _dev(lse_part, "lse_part", f32), int(o_part.shape[0]) if o_part is not None else 0,
+        _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32), _stream(stream))
     _check("mla_decode_paged_planned", st)
 
 

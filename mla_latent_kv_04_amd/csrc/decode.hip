@@ -16,9 +16,12 @@
 //   tile      = TT consecutive tokens of one paged block, staged in LDS with
 //               direct global->LDS loads, double buffered, shared by all waves.
 // Softmax is online (running max / sum per head, lanes of one head reduce with
-// cross-lane permutes); the running max is only moved when a score exceeds it
-// by more than 2^8, so rescaling the accumulators is rare and the result is
-// unchanged (the same reference max is used for the sum and the output).
+// cross-lane permutes).  The running max is only moved when a score exceeds it
+// by more than RESCALE_LOG2 (log2 units), so rescaling the accumulators is
+// rare.  The sum and the output use the same reference, so the result is the
+// same in exact arithmetic; in rounding it is not: under a stale reference the
+// key that sets the maximum gets a weight above 1 that is rounded to bf16
+// like every other weight, instead of exactly 1.
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -26,7 +29,10 @@ namespace mla {
 
 namespace {
 
-constexpr float RESCALE_LOG2 = 8.0f;   // lazy-rescale threshold in log2 units
+#ifndef MLA_RESCALE_LOG2
+#define MLA_RESCALE_LOG2 8.0f
+#endif
+constexpr float RESCALE_LOG2 = MLA_RESCALE_LOG2;   // lazy-rescale threshold in log2 units
 constexpr float NEG_BIG = -1.0e30f;    // finite "no key yet" running max
 
 template <class E, int HW_, int NWH_, int NWT_, int TT_>
@@ -112,13 +118,14 @@ template <class E, class C>
 __global__ void __launch_bounds__(C::THREADS, 1) decode_kernel(
     const typename E::storage* __restrict__ q_lat, const typename E::storage* __restrict__ cache,
     int num_blocks, const int* __restrict__ table, int max_blocks, const int* __restrict__ seq_lens,
-    int q_len, int n_h, int n_rows, float scale_log2, int S, const int4* __restrict__ work,
+    int q_len, int n_h, int n_rows, int n_parts, float scale_log2, int S,
+    const int4* __restrict__ work,
     float* __restrict__ o_lat, float* __restrict__ lse, float* __restrict__ o_part,
     float* __restrict__ lse_part) {
   __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
   const int lane = lane_id(), wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
   const int wh = wave % C::NWH, wt = wave / C::NWH;
-  const WorkItem wi = decode_item(blockIdx.x, work, n_rows, q_len, S, seq_lens, max_blocks);
+  const WorkItem wi = decode_item(blockIdx.x, work, n_rows, n_parts, q_len, S, seq_lens, max_blocks);
   if (!wi.valid) return;
   const int b = wi.b, m = wi.m, kb = wi.kb, ke = wi.ke;
   const int head0 = blockIdx.y * C::HG + wh * C::HW;  // this wave's first head
@@ -333,26 +340,27 @@ template <class E, class C>
 hipError_t launch(const void* q_lat, const void* cache, int num_blocks, const int* table,
                   int max_blocks, const int* seq_lens, int B, int q_len, int n_h, float scale,
                   int S, const int* work, int n_work, float* o_lat, float* lse, float* o_part,
-                  float* lse_part, hipStream_t stream) {
+                  float* lse_part, int n_parts, hipStream_t stream) {
   const long n_items = work != nullptr ? (long)n_work : (long)B * q_len * S;
   if (n_items == 0) return hipSuccess;
   dim3 grid((unsigned)n_items, n_h / C::HG), block(C::THREADS);
   using T = typename E::storage;
   hipLaunchKernelGGL((decode_kernel<E, C>), grid, block, 0, stream, (const T*)q_lat,
                      (const T*)cache, num_blocks, table, max_blocks, seq_lens, q_len, n_h,
-                     B * q_len, scale * LOG2E, S, (const int4*)work, o_lat, lse, o_part,
+                     B * q_len, n_parts, scale * LOG2E, S, (const int4*)work, o_lat, lse, o_part,
                      lse_part);
   return hipGetLastError();
 }
 
 #define MLA_DECODE_ARGS q_lat, cache, num_blocks, table, max_blocks, seq_lens, B, q_len, n_h, \
-                        scale, S, work, n_work, o_lat, lse, o_part, lse_part, stream
+                        scale, S, work, n_work, o_lat, lse, o_part, lse_part, n_parts, stream
 
 template <class E, int TT>
 hipError_t dispatch_heads(const void* q_lat, const void* cache, int num_blocks, const int* table,
                           int max_blocks, const int* seq_lens, int B, int q_len, int n_h,
                           float scale, int S, const int* work, int n_work, float* o_lat,
-                          float* lse, float* o_part, float* lse_part, hipStream_t stream) {
+                          float* lse, float* o_part, float* lse_part, int n_parts,
+                          hipStream_t stream) {
   constexpr int NWT16 = TT / 16 < 4 ? TT / 16 : 4;   // token slices for a lone head block
   if (n_h == 16) return launch<E, Cfg<E, 16, 1, NWT16, TT>>(MLA_DECODE_ARGS);
   if (n_h == 32) return launch<E, Cfg<E, 16, 2, 2, TT>>(MLA_DECODE_ARGS);
@@ -365,11 +373,11 @@ hipError_t launch_decode(const void* q_lat, const void* cache, int num_blocks, c
                          int max_blocks, const int* seq_lens, int B, int q_len, int n_h,
                          int dtype, float scale, int S, const int* work, int n_work,
                          const int* lists, int n_lists, float* o_lat, float* lse, float* o_part,
-                         float* lse_part, hipStream_t stream) {
+                         float* lse_part, int n_parts, hipStream_t stream) {
   if (dtype == 1 && n_h % 64 == 0)
     return launch_decode_h64(q_lat, cache, num_blocks, table, max_blocks, seq_lens, B, q_len,
                              n_h, scale, S, work, n_work, lists, n_lists, o_lat, lse, o_part,
-                             lse_part, stream);
+                             lse_part, n_parts, stream);
   if (dtype == 1) return dispatch_heads<BF16, 64>(MLA_DECODE_ARGS);
   return dispatch_heads<F32, 32>(MLA_DECODE_ARGS);
 }

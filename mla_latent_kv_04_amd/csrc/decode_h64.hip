@@ -58,7 +58,10 @@ namespace mla {
 
 namespace {
 
-constexpr float RESCALE_LOG2 = 8.0f;  // lazy-rescale threshold (log2 units)
+#ifndef MLA_RESCALE_LOG2
+#define MLA_RESCALE_LOG2 8.0f
+#endif
+constexpr float RESCALE_LOG2 = MLA_RESCALE_LOG2;  // lazy-rescale threshold (log2 units)
 constexpr float NEG_BIG = -1.0e30f;   // finite "no key yet" running max
 
 constexpr int NTHREADS = 512;                // 4 score waves + 4 value waves
@@ -95,14 +98,14 @@ static_assert(SMEM <= 163840, "LDS budget");
 static_assert(TT * RSLOTS * 16 == STAGE && NINST % 4 == 0, "a tile is whole load instructions");
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS loads.  Instruction j (0..36) of a tile fills stage slots
-// 64j..64j+63; lane l's slot s = 64j + l is chunk s % 73 of token s / 73, read
-// from byte token * 1152 + chunk * 16 of the tile's half block (the pad chunk
-// re-reads chunk 71, and the slots past the tile, which land in the stage's
-// spare bytes, re-read the last chunk).  Consecutive lanes read consecutive
-// 16-byte chunks of a row, which the address path coalesces; lanes spread over
-// rows 1152 bytes apart would be served at about a quarter of the rate.  Value
-// wave wp issues instructions j = wp + 4i.
+// Direct-to-LDS loads.  Instruction j (0..35) of a tile fills stage slots
+// 64j..64j+63; slot s holds position s % 72 of token row s / 72 (72 16-byte
+// chunks per 1152-byte row, no padding), and lane l of instruction j reads the
+// chunk that the row's swizzle (below) places at slot 64j + l.  The swizzle
+// only permutes chunks inside aligned 256-byte groups, so the 16 lanes of a
+// group read one contiguous 256-byte piece of a row, which the address path
+// coalesces; lanes spread over rows 1152 bytes apart would be served at about
+// a quarter of the rate.  Value wave wp issues instructions j = wp + 4i.
 //
 // The instruction is written out (scalar base + 32-bit lane offset, M0 = LDS
 // destination; one wait state between the M0 write and its use).  Left to the
@@ -256,7 +259,7 @@ __device__ __forceinline__ bool stage_ids(int* ids, const int* trow, int blk0, i
 __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
     const uint16_t* __restrict__ q_lat, const uint16_t* __restrict__ cache, int num_blocks,
     const int* __restrict__ table, int max_blocks, const int* __restrict__ seq_lens, int q_len,
-    int n_h, int n_items, int n_rows, float scale_log2, int S, const int4* __restrict__ work,
+    int n_h, int n_items, int n_rows, int n_parts, float scale_log2, int S, const int4* __restrict__ work,
     const int* __restrict__ lists, int n_lists, float* __restrict__ o_lat,
     float* __restrict__ lse, float* __restrict__ o_part, float* __restrict__ lse_part) {
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -318,7 +321,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
     constexpr int KPF = 3;  // K fragments are read KPF steps ahead
 
     for (int item = i_begin; item < i_end; ++item) {
-      const WorkItem wi = decode_item(item, work, n_rows, q_len, S, seq_lens, max_blocks);
+      const WorkItem wi = decode_item(item, work, n_rows, n_parts, q_len, S, seq_lens, max_blocks);
       if (!uniform(wi.valid)) continue;
       const int kb = uniform(wi.kb), ke = uniform(wi.ke);
       const int* const trow = table + (long)wi.b * max_blocks;
@@ -498,7 +501,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
     const i16x8_t ones = lds_b128(smem + OFF_ONES);
 
     for (int item = i_begin; item < i_end; ++item) {
-      const WorkItem wi = decode_item(item, work, n_rows, q_len, S, seq_lens, max_blocks);
+      const WorkItem wi = decode_item(item, work, n_rows, n_parts, q_len, S, seq_lens, max_blocks);
       if (!uniform(wi.valid)) continue;
       const int kb = uniform(wi.kb), ke = uniform(wi.ke);
       const int* const trow = table + (long)wi.b * max_blocks;
@@ -646,7 +649,7 @@ hipError_t launch_decode_h64(const void* q_lat, const void* cache, int num_block
                              const int* table, int max_blocks, const int* seq_lens, int B,
                              int q_len, int n_h, float scale, int S, const int* work, int n_work,
                              const int* lists, int n_lists, float* o_lat, float* lse,
-                             float* o_part, float* lse_part, hipStream_t stream) {
+                             float* o_part, float* lse_part, int n_parts, hipStream_t stream) {
   const long n_items = work != nullptr ? (long)n_work : (long)B * q_len * S;
   const long n_units = lists != nullptr ? (long)n_lists : n_items;
   const int ngroups = n_h / HG;
@@ -654,7 +657,7 @@ hipError_t launch_decode_h64(const void* q_lat, const void* cache, int num_block
   if (wgs == 0 || n_items == 0) return hipSuccess;
   hipLaunchKernelGGL(decode_h64_kernel, dim3((unsigned)wgs), dim3(NTHREADS), 0, stream,
                      (const uint16_t*)q_lat, (const uint16_t*)cache, num_blocks, table,
-                     max_blocks, seq_lens, q_len, n_h, (int)n_items, B * q_len, scale * LOG2E, S,
+                     max_blocks, seq_lens, q_len, n_h, (int)n_items, B * q_len, n_parts, scale * LOG2E, S,
                      (const int4*)work, lists, n_lists, o_lat, lse, o_part, lse_part);
   return hipGetLastError();
 }

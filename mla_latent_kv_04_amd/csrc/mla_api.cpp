@@ -93,10 +93,12 @@ int32_t mla_decode_paged(const void* q_lat, const void* kv_cache, int32_t num_bl
   }
   if (!aligned16(q_lat) || !aligned16(kv_cache) || !aligned16(o_out) || !aligned4(l_out))
     return MLA_ERR_ALIGN;
+  const int64_t n_parts = num_splits > 1 ? (int64_t)B * q_len * num_splits : 0;
+  if (n_parts > 0x7fffffffLL) return MLA_ERR_SHAPE;
   return hip_status(mla::launch_decode(q_lat, kv_cache, num_blocks, block_table, max_blocks,
                                        seq_lens, B, q_len, n_h, dtype, softmax_scale, num_splits,
                                        nullptr, 0, nullptr, 0, o_lat, lse, o_part, lse_part,
-                                       (hipStream_t)stream));
+                                       (int)n_parts, (hipStream_t)stream));
 }
 
 int32_t mla_plan_decode(const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t block_size,
@@ -214,23 +216,24 @@ int32_t mla_decode_paged_planned(const void* q_lat, const void* kv_cache, int32_
                                  int32_t max_blocks, int32_t B, int32_t q_len, int32_t n_h,
                                  int32_t dtype, float softmax_scale, const int32_t* work,
                                  int32_t n_work, const int32_t* lists, int32_t n_lists,
-                                 float* o_part, float* lse_part, float* o_lat, float* lse,
-                                 void* stream) {
+                                 float* o_part, float* lse_part, int32_t n_parts, float* o_lat,
+                                 float* lse, void* stream) {
   if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
   if (B < 0 || q_len < 1 || num_blocks < 1 || max_blocks < 1 || block_size != MLA_BLOCK ||
-      !decode_heads_ok(n_h) || n_work < 0 || !(softmax_scale > 0.0f) ||
+      !decode_heads_ok(n_h) || n_work < 0 || n_parts < 0 || !(softmax_scale > 0.0f) ||
       (lists && n_lists < 1))
     return MLA_ERR_SHAPE;
   if ((int64_t)B * q_len > 0x7fffffffLL) return MLA_ERR_SHAPE;
   if (n_work == 0 || B == 0) return MLA_OK;
   if (!q_lat || !kv_cache || !block_table || !work || !o_lat || !lse) return MLA_ERR_NULL;
+  if (n_parts > 0 && (!o_part || !lse_part)) return MLA_ERR_NULL;
   if (!aligned16(q_lat) || !aligned16(kv_cache) || !aligned16(o_lat) || !aligned4(lse) ||
       !aligned16(work) || (o_part && !aligned16(o_part)) || (lse_part && !aligned4(lse_part)))
     return MLA_ERR_ALIGN;
   return hip_status(mla::launch_decode(q_lat, kv_cache, num_blocks, block_table, max_blocks,
                                        nullptr, B, q_len, n_h, dtype, softmax_scale, 1, work,
                                        n_work, lists, lists ? n_lists : 0, o_lat, lse, o_part,
-                                       lse_part, (hipStream_t)stream));
+                                       lse_part, n_parts, (hipStream_t)stream));
 }
 
 int32_t mla_combine_planned(const float* o_part, const float* lse_part, const int32_t* split,

@@ -171,14 +171,17 @@ struct WorkItem {
 
 // Uniform split-KV (work == nullptr): item = (b * q_len + m) * S + s, split s of
 // sequence b's blocks cut into S runs of ceil(nblk / S) blocks.  Planned
-// (work != nullptr): work[item] = {row, key_begin, key_end, slot}.
-__device__ __forceinline__ WorkItem decode_item(int item, const int4* work, int n_rows, int q_len,
-                                                int S, const int* seq_lens, int max_blocks) {
+// (work != nullptr): work[item] = {row, key_begin, key_end, slot}; an item
+// whose row is outside [0, n_rows) or whose slot is >= n_parts is skipped
+// (nothing is written for it).
+__device__ __forceinline__ WorkItem decode_item(int item, const int4* work, int n_rows,
+                                                int n_parts, int q_len, int S,
+                                                const int* seq_lens, int max_blocks) {
   WorkItem w;
   const int cap = max_blocks * BLOCK;
   if (work != nullptr) {
     const int4 v = work[item];
-    w.valid = v.x >= 0 && v.x < n_rows;
+    w.valid = v.x >= 0 && v.x < n_rows && v.w < n_parts;
     const int row = w.valid ? v.x : 0;
     w.b = row / q_len;
     w.m = row % q_len;

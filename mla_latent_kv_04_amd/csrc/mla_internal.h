@@ -17,7 +17,8 @@ hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w
 
 // Paged attention.  Uniform splits when work == nullptr (S splits per row,
 // partials at row (b * S + s) * q_len + m when S > 1), else a work list of
-// n_work int4 {row, key_begin, key_end, slot}.  With lists != nullptr the
+// n_work int4 {row, key_begin, key_end, slot}; n_parts bounds the slots (an
+// item with slot >= n_parts is skipped).  With lists != nullptr the
 // items lists[k] .. lists[k+1]-1 (k < n_lists) are run in order by one
 // workgroup per head group (a scheduling hint: kernels that do not use it run
 // one item per workgroup, with the same results).
@@ -25,14 +26,14 @@ hipError_t launch_decode(const void* q_lat, const void* cache, int num_blocks, c
                          int max_blocks, const int* seq_lens, int B, int q_len, int n_h,
                          int dtype, float scale, int S, const int* work, int n_work,
                          const int* lists, int n_lists, float* o_lat, float* lse, float* o_part,
-                         float* lse_part, hipStream_t stream);
+                         float* lse_part, int n_parts, hipStream_t stream);
 
 // bf16, n_h a multiple of 64 (decode_h64.hip); same arguments.
 hipError_t launch_decode_h64(const void* q_lat, const void* cache, int num_blocks,
                              const int* table, int max_blocks, const int* seq_lens, int B,
                              int q_len, int n_h, float scale, int S, const int* work, int n_work,
                              const int* lists, int n_lists, float* o_lat, float* lse,
-                             float* o_part, float* lse_part, hipStream_t stream);
+                             float* o_part, float* lse_part, int n_parts, hipStream_t stream);
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int B, int S, int q_len,
                           int n_h, float* o_lat, float* lse, hipStream_t stream);

@@ -50,7 +50,7 @@ import numpy as np
 __all__ = [
     "rope_rotate", "mla_attention_naive", "kv_cache_rows", "absorb_query",
     "latent_attention", "split_ranges", "combine_splits", "out_projection",
-    "visible_keys", "mla_reference_problem", "rms_norm", "kv_produce", "q_produce",
+    "visible_keys", "rms_norm", "kv_produce", "q_produce",
     "q_produce_direct", "o_projection",
 ]
 
@@ -262,24 +262,6 @@ def out_projection(o_lat, w_uv):
     for i in range(n_h):
         out[:, i, :] = o_lat[:, i, :] @ w_uv[i].T
     return out
-
-
-def mla_reference_problem(seq_c_kv, seq_k_r, q_nope, q_rope, w_uk, w_uv, seq_len: int,
-                          q_len: int, q_pos, scale: float, base: float, heads=None):
-    """Non-absorbed reference of one sequence's q_len query rows.
-
-    Keys sit at positions 0..seq_len-1 (R4).  ``heads`` optionally restricts
-    the evaluation to a subset of heads (for sampled checks at full size).
-    Returns (out, lse, o_lat) for the selected heads.
-    """
-    L = int(seq_len)
-    if heads is not None:
-        heads = np.asarray(heads)
-        q_nope, q_rope = q_nope[:, heads], q_rope[:, heads]
-        w_uk, w_uv = w_uk[heads], w_uv[heads]
-    return mla_attention_naive(seq_c_kv[:L], seq_k_r[:L], q_nope, q_rope, w_uk, w_uv,
-                               np.arange(L), np.asarray(q_pos), visible_keys(L, q_len),
-                               scale, base)
 
 
 # ---------------------------------------------------------------- producers

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
     for s in range(6):
         assert len(B.status_string(s)) > 0
     assert B.status_string(99) == "unknown status"
@@ -69,6 +69,23 @@ def test_decode_rejects_bad_arguments(lib):
     assert run(S=4) == 1                  # split path needs partial buffers
     assert run(q_lat=MISALIGNED) == 3
     assert run(B=0) == 0                  # nothing to do
+
+
+def test_planned_decode_needs_partial_buffers_for_its_slots(lib):
+    """A plan whose items write partial rows (n_parts > 0) must come with the
+    partial buffers; negative counts are refused (nothing is launched)."""
+    call = lib.mla_decode_paged_planned
+
+    def run(op=FAKE, lp=FAKE, n_parts=4, n_work=3):
+        return call(FAKE, FAKE, 4, 64, FAKE, 4, 2, 1, 128, 1, 0.07, FAKE, n_work, FAKE, 2,
+                    op, lp, n_parts, FAKE, FAKE, None)
+
+    assert run(op=NULL) == 1
+    assert run(lp=NULL) == 1
+    assert run(op=NULL, lp=NULL, n_parts=-1) == 2
+    assert run(n_work=-1) == 2
+    assert run(op=MISALIGNED) == 3
+    assert run(n_work=0) == 0             # nothing to do
 
 
 def test_other_entry_points_reject_bad_arguments(lib):
