@@ -47,7 +47,8 @@
  *   the kernels skip entries that point outside the cache (a block id outside
  *   [0, num_blocks) contributes no keys and receives no rows) instead of
  *   faulting.  No C++ exception crosses this interface.  All entry points are
- *   thread-safe: the library holds no mutable global state.
+ *   thread-safe: the library holds no mutable global state, apart from the
+ *   per-device scratch array of mla_decode_paged_noalloc (see there).
  */
 #ifndef MLA_LATENT_KV_MLA_H
 #define MLA_LATENT_KV_MLA_H
@@ -76,7 +77,8 @@ enum mla_status {
   MLA_ERR_SHAPE = 2,  /* a size is out of range or inconsistent */
   MLA_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned */
   MLA_ERR_DTYPE = 4,  /* unknown dtype */
-  MLA_ERR_HIP = 5     /* the HIP runtime refused a launch */
+  MLA_ERR_HIP = 5,    /* the HIP runtime refused a launch */
+  MLA_ERR_SCRATCH = 6 /* the problem needs more than the library's fixed scratch */
 };
 
 /* Static text for a status code (never NULL). */
@@ -400,6 +402,31 @@ int32_t mla_prefill_mha(const void* q_nope, const void* q_rope, const int32_t* q
                         int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t q_len,
                         int32_t n_h, int32_t dtype, float scale, float rope_base, float* out,
                         float* lse, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_paged_noalloc - for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): mla_decode_paged followed, when num_splits > 1, by
+ * mla_splitkv_combine, with the split partials kept in a device array that
+ * the library itself holds, MLA_NOALLOC_SCRATCH_BYTES per GPU, from the
+ * first call on that GPU until the process ends.  The caller passes only the
+ * inputs and the merged outputs o_lat [B, q_len, n_h, 512] and lse
+ * [B, q_len, n_h] (fp32, device).  Arguments, layouts and results are those
+ * of mla_decode_paged with num_splits == 1 (the result of a split call
+ * equals mla_decode_paged with num_splits partials merged by
+ * mla_splitkv_combine).  The partials take B * num_splits * q_len * n_h *
+ * 513 * 4 bytes; a call that needs more than MLA_NOALLOC_SCRATCH_BYTES
+ * returns MLA_ERR_SCRATCH with nothing enqueued.  No allocation, free or
+ * synchronisation happens.  All calls on one GPU share its array: calls that
+ * overlap on one GPU (other streams or host threads) race and must be
+ * ordered by the caller.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+int32_t mla_decode_paged_noalloc(const void* q_lat, const void* kv_cache, int32_t num_blocks,
+                                 int32_t block_size, const int32_t* block_table,
+                                 int32_t max_blocks, const int32_t* seq_lens, int32_t B,
+                                 int32_t q_len, int32_t n_h, int32_t dtype, float softmax_scale,
+                                 int32_t num_splits, float* o_lat, float* lse, void* stream);
 
 #ifdef __cplusplus
 }

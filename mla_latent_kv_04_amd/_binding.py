@@ -24,7 +24,7 @@ _EXPORTS = ("mla_status_string", "mla_abi_version", "mla_kv_append", "mla_absorb
             "mla_out_proj_planned", "mla_kv_produce_workspace", "mla_kv_produce",
             "mla_q_produce_workspace", "mla_q_produce", "mla_q_produce_direct",
             "mla_o_proj_workspace", "mla_o_proj",
-            "mla_prefill_mha_workspace", "mla_prefill_mha")
+            "mla_prefill_mha_workspace", "mla_prefill_mha", "mla_decode_paged_noalloc")
 
 
 class MLAError(RuntimeError):
@@ -78,6 +78,8 @@ def load() -> ctypes.CDLL:
         "mla_o_proj_workspace": (ctypes.c_int64, [_I, _I, _I, _I]),
         "mla_o_proj": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_int64, _P]),
         "mla_prefill_mha_workspace": (ctypes.c_int64, [_I, _I]),
+        "mla_decode_paged_noalloc": (_I, [_P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F, _I,
+                                          _P, _P, _P]),
         "mla_prefill_mha": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F,
                                  _F, _P, _P, _P, ctypes.c_int64, _P]),
     }
@@ -513,3 +515,33 @@ def mla_o_proj(out, w_o, u, workspace=None, stream=None):
                            _dev(u, "u"), _dev(workspace, "workspace"),
                            0 if workspace is None else int(workspace.numel()), _stream(stream))
     _check("mla_o_proj", st)
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+
+
+def mla_decode_paged_noalloc(q_lat, kv_cache, block_table, seq_lens, q_len, softmax_scale,
+                             num_splits, o_lat, lse, stream=None):
+    """mla_decode_paged (+ mla_splitkv_combine) with the split partials in the
+    library's own per-device scratch array (see mla.h): no workspace argument."""
+    torch = _torch()
+    dt = _dtype_code(q_lat)
+    if kv_cache.dtype != q_lat.dtype:
+        raise TypeError("kv_cache dtype differs from q_lat")
+    B = int(seq_lens.shape[0])
+    n_h = int(q_lat.shape[-2])
+    if q_lat.shape[-1] != ROW or q_lat.numel() != B * q_len * n_h * ROW:
+        raise ValueError("q_lat must hold [B, q_len, n_h, 576]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    rows = B * q_len * n_h
+    if o_lat.numel() != rows * D_C or lse.numel() != rows:
+        raise ValueError("o_lat / lse must hold [B, q_len, n_h, 512] / [B, q_len, n_h]")
+    f32 = torch.float32
+    st = load().mla_decode_paged_noalloc(
+        _dev(q_lat, "q_lat"), _dev(kv_cache, "kv_cache"), int(kv_cache.shape[0]),
+        int(kv_cache.shape[1]), _dev(block_table, "block_table", torch.int32),
+        int(block_table.shape[1]), _dev(seq_lens, "seq_lens", torch.int32), B, int(q_len), n_h,
+        dt, float(softmax_scale), int(num_splits), _dev(o_lat, "o_lat", f32),
+        _dev(lse, "lse", f32), _stream(stream))
+    _check("mla_decode_paged_noalloc", st)

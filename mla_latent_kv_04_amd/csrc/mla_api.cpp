@@ -34,6 +34,7 @@ const char* mla_status_string(int32_t status) {
     case MLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MLA_ERR_DTYPE: return "unknown dtype";
     case MLA_ERR_HIP: return "the HIP runtime refused a launch";
+    case MLA_ERR_SCRATCH: return "the problem needs more than the library's fixed scratch array";
     default: return "unknown status";
   }
 }

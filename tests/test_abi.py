@@ -36,8 +36,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_abi_version_and_status_strings(lib):
     assert lib.mla_abi_version() == 2
-    for s in range(6):
+    for s in range(7):
         assert len(B.status_string(s)) > 0
+    assert "scratch" in B.status_string(6)
     assert B.status_string(99) == "unknown status"
 
 
@@ -86,6 +87,17 @@ def test_planned_decode_needs_partial_buffers_for_its_slots(lib):
     assert run(n_work=-1) == 2
     assert run(op=MISALIGNED) == 3
     assert run(n_work=0) == 0             # nothing to do
+
+
+def test_noalloc_refuses_sizes_beyond_its_scratch_without_a_gpu(lib):
+    """The partials of B=128, S=4, 128 heads (134 MB) exceed the fixed 64 MiB
+    array: MLA_ERR_SCRATCH, decided on the host before any HIP call."""
+    assert lib.mla_decode_paged_noalloc(FAKE, FAKE, 4, 64, FAKE, 4, FAKE, 128, 1, 128, 1, 0.07,
+                                        4, FAKE, FAKE, None) == 6
+    assert lib.mla_decode_paged_noalloc(FAKE, FAKE, 4, 64, FAKE, 4, FAKE, 1, 1, 48, 1, 0.07,
+                                        2, FAKE, FAKE, None) == 2
+    assert lib.mla_decode_paged_noalloc(FAKE, FAKE, 4, 64, FAKE, 4, FAKE, 1, 1, 128, 1, 0.07,
+                                        2, NULL, FAKE, None) == 1
 
 
 def test_other_entry_points_reject_bad_arguments(lib):
