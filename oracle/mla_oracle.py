@@ -42,13 +42,26 @@ Readings where the pages are silent or garbled:
   R10 a model that does not compress its queries (V2-Lite: blog, the V2-Lite
      paragraph) projects both query parts straight from the hidden state,
      q^C = W^QC h (eq. 1's W^Q, per-head rows) and q^R = W^QR h.
+  R11 YaRN (blog §3.1.3: applied to the decoupled RoPE key, scale 40, the two
+     ramp parameters 1 and 32, target context 160K) is read as YaRN's
+     interpolation by parts on the RoPE pair frequencies: with the original
+     context L0 = 4096 (the blog extends a 4K window; 40 x 4096 = 163,840 is
+     the stated 160K), pair k's frequency theta_k = base^(-2k/d) completes
+     r_k = L0 theta_k / (2 pi) turns over L0 positions; a ramp
+     g_k = clip((r_k - alpha) / (beta - alpha), 0, 1) with alpha = 1,
+     beta = 32 keeps fast pairs (g = 1) and divides slow pairs by the scale
+     (g = 0): theta'_k = (1 - g_k) theta_k / s + g_k theta_k.  The same
+     frequencies rotate q^R (a score depends on the key's and the query's
+     rotation together).  The blog's attention-entropy factor is not printed
+     (its formula is missing from the page): it multiplies every score, so it
+     is part of the softmax scale the caller passes, and it is 1 here.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = [
-    "rope_rotate", "mla_attention_naive", "kv_cache_rows", "absorb_query",
+    "rope_rotate", "rope_theta", "yarn_theta", "mla_attention_naive", "kv_cache_rows", "absorb_query",
     "latent_attention", "split_ranges", "combine_splits", "out_projection",
     "visible_keys", "rms_norm", "kv_produce", "q_produce",
     "q_produce_direct", "o_projection",
@@ -57,13 +70,33 @@ __all__ = [
 F64 = np.float64
 
 
-def rope_rotate(x, pos, base: float):
+def rope_theta(d: int, base: float):
+    """Pair frequencies of plain RoPE (reading R2): theta_k = base^(-2k/d)."""
+    k = np.arange(d // 2, dtype=F64)
+    return float(base) ** (-2.0 * k / d)
+
+
+def yarn_theta(d: int, base: float, scale: float, alpha: float, beta: float, orig_ctx: int):
+    """Pair frequencies after YaRN's interpolation by parts (reading R11).
+
+    r_k = orig_ctx * theta_k / (2 pi) is the number of turns pair k makes
+    over the original context; g_k = clip((r_k - alpha) / (beta - alpha), 0, 1);
+    theta'_k = (1 - g_k) * theta_k / scale + g_k * theta_k.
+    """
+    theta = rope_theta(d, base)
+    r = float(orig_ctx) * theta / (2.0 * np.pi)
+    g = np.clip((r - float(alpha)) / (float(beta) - float(alpha)), 0.0, 1.0)
+    return (1.0 - g) * theta / float(scale) + g * theta
+
+
+def rope_rotate(x, pos, base: float, theta=None):
     """Apply the position rotation R_pos to the trailing axis of ``x``.
 
     blog §2.2.2: RoPE multiplies a vector by a position-dependent rotation
     matrix so that (R_m q)^T (R_n k) depends on n - m only.  Reading R2: the
     matrix is block diagonal with 2x2 rotations on adjacent pairs, pair k
-    turned by angle pos * base^(-2k/d), d = x.shape[-1].
+    turned by angle pos * theta_k, theta_k = base^(-2k/d), d = x.shape[-1]
+    (or the given pair frequencies ``theta``, e.g. YaRN's, reading R11).
 
     ``pos`` broadcasts against ``x.shape[:-1]``.
     """
@@ -73,8 +106,9 @@ def rope_rotate(x, pos, base: float):
         raise ValueError("RoPE width must be even")
     if d == 0:
         return x.copy()
-    k = np.arange(d // 2, dtype=F64)
-    theta = float(base) ** (-2.0 * k / d)
+    theta = rope_theta(d, base) if theta is None else np.asarray(theta, dtype=F64)
+    if theta.shape != (d // 2,):
+        raise ValueError("theta must hold one frequency per pair")
     ang = np.asarray(pos, dtype=F64)[..., None] * theta
     c, s = np.cos(ang), np.sin(ang)
     even, odd = x[..., 0::2], x[..., 1::2]
@@ -103,7 +137,7 @@ def _softmax_two_pass(s):
 
 
 def mla_attention_naive(c_kv, k_r, q_nope, q_rope, w_uk, w_uv, key_pos, q_pos,
-                        n_visible, scale: float, base: float):
+                        n_visible, scale: float, base: float, theta=None):
     """MLA attention of one sequence in the literal, non-absorbed form.
 
     Inputs (any float type, used as float64):
@@ -112,6 +146,7 @@ def mla_attention_naive(c_kv, k_r, q_nope, q_rope, w_uk, w_uv, key_pos, q_pos,
       q_nope [M, n_h, d_h], q_rope [M, n_h, d_R]  the M query rows
       w_uk, w_uv [n_h, d_h, d_c]
       key_pos [L], q_pos [M], n_visible [M] (row m sees keys 0..n_visible[m]-1)
+      theta: optional RoPE pair frequencies (default base^(-2k/d_R))
     Steps, per head i:
       k^C_{j,i} = W^UK_i c^KV_j and v^C_{j,i} = W^UV_i c^KV_j  (eq. 10, 11)
       k^R_j = R_{pos j} k_r_j, q^R_i = R_{q pos} q_rope_i       (blog §2.2.2)
@@ -128,8 +163,8 @@ def mla_attention_naive(c_kv, k_r, q_nope, q_rope, w_uk, w_uv, key_pos, q_pos,
     w_uv = np.asarray(w_uv, F64)
     M, n_h, d_h = q_nope.shape
     d_c = c_kv.shape[1]
-    k_rot = rope_rotate(k_r, np.asarray(key_pos), base)                  # [L, d_R]
-    q_rot = rope_rotate(q_rope, np.asarray(q_pos)[:, None], base)        # [M, n_h, d_R]
+    k_rot = rope_rotate(k_r, np.asarray(key_pos), base, theta)           # [L, d_R]
+    q_rot = rope_rotate(q_rope, np.asarray(q_pos)[:, None], base, theta) # [M, n_h, d_R]
     out = np.zeros((M, n_h, d_h))
     o_lat = np.zeros((M, n_h, d_c))
     lse = np.full((M, n_h), -np.inf)
@@ -157,17 +192,17 @@ def mla_attention_naive(c_kv, k_r, q_nope, q_rope, w_uk, w_uv, key_pos, q_pos,
 # the query side and W^UV to the output side).
 # ---------------------------------------------------------------------------
 
-def kv_cache_rows(c_kv, k_r, pos, base: float):
+def kv_cache_rows(c_kv, k_r, pos, base: float, theta=None):
     """The cached row of each token: [c^KV_j ; R_{pos j} k_r_j] (readings R3, R4).
 
     blog §2.2.2: per token the cache keeps c^KV and the already rotated k^R,
     (d_c + d_R) elements.  Returns float64 [N, d_c + d_R].
     """
     c_kv = np.asarray(c_kv, F64)
-    return np.concatenate([c_kv, rope_rotate(k_r, np.asarray(pos), base)], axis=1)
+    return np.concatenate([c_kv, rope_rotate(k_r, np.asarray(pos), base, theta)], axis=1)
 
 
-def absorb_query(q_nope, q_rope, w_uk, q_pos, base: float):
+def absorb_query(q_nope, q_rope, w_uk, q_pos, base: float, theta=None):
     """Latent-space query of every row and head: [W^UK_i^T q_nope_i ; R_p q_rope_i].
 
     By eq. 10, q_nope_i . k^C_{j,i} = q_nope_i . (W^UK_i c_j) = (W^UK_i^T q_nope_i) . c_j,
@@ -180,7 +215,7 @@ def absorb_query(q_nope, q_rope, w_uk, q_pos, base: float):
     q_abs = np.empty((T, n_h, w_uk.shape[2]))
     for i in range(n_h):
         q_abs[:, i, :] = q_nope[:, i, :] @ w_uk[i]      # row-vector form of W^T q
-    q_rot = rope_rotate(q_rope, np.asarray(q_pos)[:, None], base)
+    q_rot = rope_rotate(q_rope, np.asarray(q_pos)[:, None], base, theta)
     return np.concatenate([q_abs, q_rot], axis=2)
 
 

@@ -91,6 +91,115 @@ def test_rope_composes_additively():
                                orc.rope_rotate(x, 345, 1e4), atol=1e-12)
 
 
+# ------------------------------------------------------------------------ YaRN
+
+YARN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "yarn_v2.json")))
+
+
+def _yarn_v2(d=64, base=10000.0):
+    return orc.yarn_theta(d, base, YARN["scale"], YARN["alpha"], YARN["beta"],
+                          YARN["original_context"])
+
+
+def test_yarn_fixture_is_consistent_with_the_stated_context():
+    # 4K window times scale 40 is the stated 160K target (160 x 1024).
+    assert YARN["original_context"] * YARN["scale"] == YARN["target_context"] == 160 * 1024
+    assert YARN["trained_context"] == 128 * 1024 <= YARN["target_context"]
+
+
+def test_yarn_scale_one_is_plain_rope():
+    for d, base in [(64, 10000.0), (16, 500.0)]:
+        np.testing.assert_allclose(orc.yarn_theta(d, base, 1.0, 1.0, 32.0, 4096),
+                                   orc.rope_theta(d, base), rtol=1e-15, atol=0)
+    x = np.random.default_rng(40).standard_normal(64)
+    th = orc.yarn_theta(64, 1e4, 1.0, 1.0, 32.0, 4096)
+    np.testing.assert_allclose(orc.rope_rotate(x, 777, 1e4, th), orc.rope_rotate(x, 777, 1e4),
+                               atol=1e-12)
+
+
+def test_yarn_keeps_fast_pairs_and_divides_slow_pairs_by_the_scale():
+    # With base 1e4, d 64 and a 4096-token window, pair k turns
+    # 4096 * 1e4^(-k/32) / (2 pi) times: 651.9 for k = 0, 0.087 for k = 31.
+    d, base, L0, s = 64, 1e4, YARN["original_context"], YARN["scale"]
+    th, yth = orc.rope_theta(d, base), _yarn_v2(d, base)
+    turns = [L0 * base ** (-2.0 * k / d) / (2 * math.pi) for k in range(d // 2)]
+    assert abs(turns[0] - 651.898646) < 1e-5 and abs(turns[31] - 0.0869) < 1e-4
+    n_fast = n_slow = 0
+    for k in range(d // 2):
+        if turns[k] >= YARN["beta"]:
+            assert yth[k] == th[k]
+            n_fast += 1
+        elif turns[k] <= YARN["alpha"]:
+            assert abs(yth[k] - th[k] / s) <= 1e-16 * th[k]
+            n_slow += 1
+        else:
+            assert th[k] / s < yth[k] < th[k]
+    # 651.9 * 10^(-k/8) >= 32 for k <= 10 and <= 1 for k >= 23: eleven pairs
+    # keep their frequency, nine are divided by s, twelve sit on the ramp
+    assert (n_fast, n_slow) == (11, 9)
+
+
+def test_yarn_ramp_endpoints_and_midpoint():
+    # d = 2 has the single pair theta_0 = 1, which turns L0 / (2 pi) times:
+    # choosing L0 puts it anywhere on the ramp between alpha and beta.
+    a, b, s = 1.0, 32.0, 40.0
+    for turns, want in [(a, 1.0 / s), (b, 1.0), ((a + b) / 2, 0.5 + 0.5 / s),
+                        (a + 0.25 * (b - a), 0.25 + 0.75 / s), (0.5, 1.0 / s), (100.0, 1.0)]:
+        got = orc.yarn_theta(2, 1e4, s, a, b, 2 * math.pi * turns)
+        assert abs(got[0] - want) < 1e-15, (turns, got, want)
+
+
+def test_yarn_ratio_falls_monotonically_with_the_pair_index():
+    th, yth = orc.rope_theta(64, 1e4), _yarn_v2()
+    ratio = yth / th
+    assert np.all(np.diff(ratio) <= 1e-15) and np.any(np.diff(ratio) < -1e-3)
+    assert ratio[0] == 1.0 and abs(ratio[-1] - 1.0 / YARN["scale"]) < 1e-15
+
+
+def test_yarn_slow_pairs_at_scaled_position_match_plain_rope():
+    # Interpolation: a pair divided by s turns at position s*p exactly as the
+    # plain pair turns at p, so positions up to s * 4096 stay inside the
+    # angles seen in training for those pairs.
+    d, s = 64, YARN["scale"]
+    th, yth = orc.rope_theta(d, 1e4), _yarn_v2(d)
+    slow = np.flatnonzero(np.abs(yth - th / s) <= 1e-16 * th)
+    fast = np.flatnonzero(yth == th)
+    x = np.random.default_rng(41).standard_normal(d)
+    for p in [1, 100, 4095]:
+        y_ext = orc.rope_rotate(x, s * p, 1e4, yth).reshape(-1, 2)
+        y_pln = orc.rope_rotate(x, p, 1e4).reshape(-1, 2)
+        y_far = orc.rope_rotate(x, s * p, 1e4).reshape(-1, 2)
+        np.testing.assert_allclose(y_ext[slow], y_pln[slow], atol=1e-10)
+        np.testing.assert_allclose(y_ext[fast], y_far[fast], atol=1e-10)
+
+
+def test_yarn_attention_is_shift_invariant_and_absorbs():
+    # One frequency table rotates queries and keys together, so a common shift
+    # of all positions leaves every output unchanged; and the absorbed chain
+    # with that table equals the non-absorbed form.
+    t = _tiny(seed=42, L=7, n_h=3, d_h=4, d_c=8, d_r=64, M=2)
+    th = _yarn_v2()
+    kp, qp, vis, sc = np.arange(7), np.array([5, 6]), np.array([6, 7]), 0.3
+    o, l, _ = orc.mla_attention_naive(**t, key_pos=kp, q_pos=qp, n_visible=vis, scale=sc,
+                                      base=1e4, theta=th)
+    o2, l2, _ = orc.mla_attention_naive(**t, key_pos=kp + 50000, q_pos=qp + 50000, n_visible=vis,
+                                     scale=sc, base=1e4, theta=th)
+    np.testing.assert_allclose(o2, o, atol=1e-9)
+    np.testing.assert_allclose(l2, l, atol=1e-9)
+    o3, _, _ = orc.mla_attention_naive(**t, key_pos=kp, q_pos=qp, n_visible=vis, scale=sc, base=1e4)
+    assert np.max(np.abs(o3 - o)) > 1e-6          # the table does change the result
+    q_lat = orc.absorb_query(t["q_nope"], t["q_rope"], t["w_uk"], qp, 1e4, th)
+    rows = orc.kv_cache_rows(t["c_kv"], t["k_r"], kp, 1e4, th)
+    o_lat, l4 = orc.latent_attention(q_lat, rows, vis, sc, 8)
+    np.testing.assert_allclose(orc.out_projection(o_lat, t["w_uv"]), o, atol=1e-12)
+    np.testing.assert_allclose(l4, l, atol=1e-12)
+
+
+def test_rope_rejects_a_table_of_the_wrong_length():
+    with pytest.raises(ValueError):
+        orc.rope_rotate(np.zeros(8), 1, 1e4, np.ones(3))
+
+
 # ------------------------------------------------------------ brute-force naive MLA
 
 def _brute_force(c_kv, k_r, q_nope, q_rope, w_uk, w_uv, key_pos, q_pos, n_vis, scale, base):
