@@ -29,8 +29,14 @@
  *   fp32; sums accumulate in fp32).  o_lat, lse, partials and the output are
  *   always fp32.
  * - RoPE (reading of blog §2.2.2, which only fixes R_m^T R_n = R_{n-m}): adjacent
- *   element pairs (x[2k], x[2k+1]) are rotated by angle pos * base^(-2k/64),
- *   k = 0..31; angles are formed in float64.
+ *   element pairs (x[2k], x[2k+1]) are rotated by angle pos * theta_k,
+ *   k = 0..31, theta_k = base^(-2k/64); angles are formed in float64.  Every
+ *   entry point that rotates takes `float rope_base` and
+ *   `const double* rope_theta`: a host array of the 32 pair frequencies
+ *   (radians per position) that, when not NULL, replaces base^(-2k/64)
+ *   (rope_base is then unused), e.g. the YaRN table of mla_rope_theta.  Use
+ *   one table for the keys and the queries of a model.  A table entry (or a
+ *   rope_base) that is not finite and positive gives MLA_ERR_SHAPE.
  * - Paged cache: kv_cache is [num_blocks, block_size, 576] elements of dtype,
  *   rows contiguous (a bf16 row is 1152 bytes = 72 x 16 bytes).  Token j of
  *   sequence b lives in block block_table[b * max_blocks + j / block_size],
@@ -59,7 +65,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 2
+#define MLA_ABI_VERSION 3
 
 #define MLA_D_C 512
 #define MLA_D_R 64
@@ -88,6 +94,29 @@ const char* mla_status_string(int32_t status);
 int32_t mla_abi_version(void);
 
 /*
+ * mla_rope_theta - RoPE pair frequencies with YaRN's interpolation by parts.
+ *
+ * DeepSeek-V2 extends its 4K context to 128K by applying YaRN to the
+ * decoupled shared key only, with scale s = 40, ramp bounds alpha = 1 and
+ * beta = 32, aiming at 160K = 40 x 4K (DeepSeek-V2 MLA blog, part 2 §3.1.3).
+ * Read as YaRN's by-parts rule: pair k of plain RoPE, f_k = base^(-2k/64),
+ * makes r_k = orig_ctx * f_k / (2 pi) turns over the original window; with
+ * g_k = clamp((r_k - alpha) / (beta - alpha), 0, 1),
+ *   theta[k] = g_k * f_k + (1 - g_k) * f_k / scale,      k = 0..31,
+ * so fast pairs (r_k >= beta) keep their frequency and slow pairs
+ * (r_k <= alpha) are slowed by s.  scale = 1 gives plain RoPE.  YaRN's
+ * attention-temperature factor multiplies every score, so it belongs in the
+ * softmax scale the caller passes to the attention entry points.
+ *
+ * theta  host, double [32] (written)
+ * Host arithmetic only: no device call.  MLA_ERR_NULL if theta is NULL;
+ * MLA_ERR_SHAPE unless base > 1, scale >= 1, 0 <= alpha < beta and
+ * orig_ctx > 0, all finite.
+ */
+int32_t mla_rope_theta(double base, double scale, double alpha, double beta, double orig_ctx,
+                       double* theta);
+
+/*
  * mla_kv_append - write n new tokens into the paged latent cache.
  *
  * The cache keeps c^KV unrotated and k^R already rotated at the token's
@@ -111,7 +140,7 @@ int32_t mla_kv_append(void* kv_cache, int32_t dtype, int32_t num_blocks, int32_t
                       const int32_t* block_table, int32_t num_seqs, int32_t max_blocks,
                       const void* c_kv, const void* k_rope,
                       const int32_t* seq_idx, const int32_t* pos, int32_t n,
-                      float rope_base, void* stream);
+                      float rope_base, const double* rope_theta, void* stream);
 
 /*
  * mla_absorb_q - latent-space queries (W^UK absorbed into the query).
@@ -130,7 +159,7 @@ int32_t mla_kv_append(void* kv_cache, int32_t dtype, int32_t num_blocks, int32_t
  */
 int32_t mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
                      const int32_t* q_pos, int32_t T, int32_t n_h, int32_t dtype,
-                     float rope_base, void* q_lat, void* stream);
+                     float rope_base, const double* rope_theta, void* q_lat, void* stream);
 
 /*
  * mla_decode_paged - attention of latent queries over the paged cache.
@@ -320,7 +349,8 @@ int64_t mla_kv_produce_workspace(int32_t T, int32_t d_model);
  */
 int32_t mla_kv_produce(const void* h, const void* w_dkv, const float* kv_gain, const void* w_kr,
                        int32_t T, int32_t d_model, int32_t dtype, float eps, float rope_base,
-                       void* kv_cache, int32_t num_blocks, int32_t block_size,
+                       const double* rope_theta, void* kv_cache, int32_t num_blocks,
+                       int32_t block_size,
                        const int32_t* block_table, int32_t num_seqs, int32_t max_blocks,
                        const int32_t* seq_idx, const int32_t* pos, void* workspace,
                        int64_t workspace_bytes, void* stream);
@@ -400,8 +430,9 @@ int32_t mla_prefill_mha(const void* q_nope, const void* q_rope, const int32_t* q
                         const void* w_uk, const void* w_uv, const void* kv_cache,
                         int32_t num_blocks, int32_t block_size, const int32_t* block_table,
                         int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t q_len,
-                        int32_t n_h, int32_t dtype, float scale, float rope_base, float* out,
-                        float* lse, void* workspace, int64_t workspace_bytes, void* stream);
+                        int32_t n_h, int32_t dtype, float scale, float rope_base,
+                        const double* rope_theta, float* out, float* lse, void* workspace,
+                        int64_t workspace_bytes, void* stream);
 
 /*
  * mla_decode_paged_noalloc - for callers that cannot allocate device memory

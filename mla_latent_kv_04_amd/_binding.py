@@ -18,9 +18,9 @@ MLA_F32, MLA_BF16 = 0, 1
 MLA_OK = 0
 D_C, D_R, D_H, ROW, BLOCK = 512, 64, 128, 576, 64
 
-_EXPORTS = ("mla_status_string", "mla_abi_version", "mla_kv_append", "mla_absorb_q",
-            "mla_decode_paged", "mla_splitkv_combine", "mla_out_proj", "mla_split_plan",
-            "mla_plan_decode", "mla_decode_paged_planned", "mla_combine_planned",
+_EXPORTS = ("mla_status_string", "mla_abi_version", "mla_rope_theta", "mla_kv_append",
+            "mla_absorb_q", "mla_decode_paged", "mla_splitkv_combine", "mla_out_proj",
+            "mla_split_plan", "mla_plan_decode", "mla_decode_paged_planned", "mla_combine_planned",
             "mla_out_proj_planned", "mla_kv_produce_workspace", "mla_kv_produce",
             "mla_q_produce_workspace", "mla_q_produce", "mla_q_produce_direct",
             "mla_o_proj_workspace", "mla_o_proj",
@@ -38,6 +38,7 @@ _lib: Optional[ctypes.CDLL] = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _F = ctypes.c_float
+_D = ctypes.c_double
 
 
 def lib_path() -> str:
@@ -56,8 +57,9 @@ def load() -> ctypes.CDLL:
     sig = {
         "mla_status_string": (ctypes.c_char_p, [_I]),
         "mla_abi_version": (_I, []),
-        "mla_kv_append": (_I, [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I, _F, _P]),
-        "mla_absorb_q": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P]),
+        "mla_rope_theta": (_I, [_D, _D, _D, _D, _D, _P]),
+        "mla_kv_append": (_I, [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I, _F, _P, _P]),
+        "mla_absorb_q": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P]),
         "mla_decode_paged": (_I, [_P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F, _I,
                                   _P, _P, _P, _P, _P]),
         "mla_splitkv_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P]),
@@ -69,8 +71,8 @@ def load() -> ctypes.CDLL:
         "mla_combine_planned": (_I, [_P, _P, _P, _I, _I, _P, _P, _P]),
         "mla_out_proj_planned": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
         "mla_kv_produce_workspace": (ctypes.c_int64, [_I, _I]),
-        "mla_kv_produce": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _F, _P, _I, _I, _P, _I, _I, _P,
-                                _P, _P, ctypes.c_int64, _P]),
+        "mla_kv_produce": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _I, _I, _P, _I, _I,
+                                _P, _P, _P, ctypes.c_int64, _P]),
         "mla_q_produce_workspace": (ctypes.c_int64, [_I, _I, _I, _I]),
         "mla_q_produce": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P,
                                ctypes.c_int64, _P]),
@@ -81,7 +83,7 @@ def load() -> ctypes.CDLL:
         "mla_decode_paged_noalloc": (_I, [_P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F, _I,
                                           _P, _P, _P]),
         "mla_prefill_mha": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F,
-                                 _F, _P, _P, _P, ctypes.c_int64, _P]),
+                                 _F, _P, _P, _P, _P, ctypes.c_int64, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -138,6 +140,21 @@ def _dev(t, name: str, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _theta(rope_theta):
+    """float64 host copy of a RoPE frequency table [32] (None stays None).
+    The caller keeps the returned array alive across the C call."""
+    if rope_theta is None:
+        return None
+    arr = np.ascontiguousarray(np.asarray(rope_theta, dtype=np.float64))
+    if arr.shape != (D_R // 2,):
+        raise ValueError("rope_theta must hold 32 pair frequencies")
+    return arr
+
+
+def _ptr(arr):
+    return None if arr is None else arr.ctypes.data_as(ctypes.c_void_p)
+
+
 def _stream(stream):
     torch = _torch()
     if stream is None:
@@ -149,8 +166,18 @@ def _stream(stream):
 # Entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
 
+def mla_rope_theta(base=10000.0, scale=1.0, alpha=1.0, beta=32.0, orig_ctx=4096.0):
+    """RoPE pair frequencies [32] with YaRN's interpolation by parts (see mla.h).
+    Host arithmetic only."""
+    out = np.zeros(D_R // 2, dtype=np.float64)
+    st = load().mla_rope_theta(float(base), float(scale), float(alpha), float(beta),
+                               float(orig_ctx), _ptr(out))
+    _check("mla_rope_theta", st)
+    return out
+
+
 def mla_kv_append(kv_cache, block_table, c_kv, k_rope, seq_idx, pos, rope_base=10000.0,
-                  stream=None):
+                  stream=None, rope_theta=None):
     """Write rows [c_kv ; R_pos k_rope] into the paged cache (see mla.h)."""
     torch = _torch()
     dt = _dtype_code(kv_cache)
@@ -164,16 +191,18 @@ def mla_kv_append(kv_cache, block_table, c_kv, k_rope, seq_idx, pos, rope_base=1
         raise ValueError("seq_idx and pos must be [n]")
     if kv_cache.dim() != 3 or kv_cache.shape[2] != ROW:
         raise ValueError("kv_cache must be [num_blocks, 64, 576]")
+    th = _theta(rope_theta)
     st = load().mla_kv_append(
         _dev(kv_cache, "kv_cache"), dt, int(kv_cache.shape[0]), int(kv_cache.shape[1]),
         _dev(block_table, "block_table", torch.int32), int(block_table.shape[0]),
         int(block_table.shape[1]), _dev(c_kv, "c_kv"), _dev(k_rope, "k_rope"),
         _dev(seq_idx, "seq_idx", torch.int32), _dev(pos, "pos", torch.int32), n,
-        float(rope_base), _stream(stream))
+        float(rope_base), _ptr(th), _stream(stream))
     _check("mla_kv_append", st)
 
 
-def mla_absorb_q(q_nope, q_rope, w_uk, q_pos, q_lat, rope_base=10000.0, stream=None):
+def mla_absorb_q(q_nope, q_rope, w_uk, q_pos, q_lat, rope_base=10000.0, stream=None,
+                 rope_theta=None):
     """q_lat = [W^UK^T q_nope ; R q_rope] per row and head (see mla.h)."""
     torch = _torch()
     dt = _dtype_code(q_nope)
@@ -185,9 +214,10 @@ def mla_absorb_q(q_nope, q_rope, w_uk, q_pos, q_lat, rope_base=10000.0, stream=N
     for name, t in (("q_rope", q_rope), ("w_uk", w_uk), ("q_lat", q_lat)):
         if t.dtype != q_nope.dtype:
             raise TypeError(f"{name} dtype differs from q_nope")
+    th = _theta(rope_theta)
     st = load().mla_absorb_q(_dev(q_nope, "q_nope"), _dev(q_rope, "q_rope"), _dev(w_uk, "w_uk"),
                              _dev(q_pos, "q_pos", torch.int32), T, n_h, dt, float(rope_base),
-                             _dev(q_lat, "q_lat"), _stream(stream))
+                             _ptr(th), _dev(q_lat, "q_lat"), _stream(stream))
     _check("mla_absorb_q", st)
 
 
@@ -370,7 +400,7 @@ def mla_kv_produce_workspace(T, d_model):
 
 
 def mla_kv_produce(h, w_dkv, kv_gain, w_kr, kv_cache, block_table, seq_idx, pos, rope_base,
-                   eps, workspace, stream=None):
+                   eps, workspace, stream=None, rope_theta=None):
     """Cache rows of new tokens from their hidden states (see mla.h)."""
     torch = _torch()
     dt = _dtype_code(h)
@@ -383,9 +413,11 @@ def mla_kv_produce(h, w_dkv, kv_gain, w_kr, kv_cache, block_table, seq_idx, pos,
         raise TypeError("h, the weights and the cache must share one dtype")
     if workspace.dtype != torch.uint8:
         raise TypeError("workspace must be a uint8 tensor")
+    th = _theta(rope_theta)
     st = load().mla_kv_produce(
         _dev(h, "h"), _dev(w_dkv, "w_dkv"), _dev(kv_gain, "kv_gain", torch.float32),
-        _dev(w_kr, "w_kr"), T, d_model, dt, float(eps), float(rope_base), _dev(kv_cache, "kv_cache"),
+        _dev(w_kr, "w_kr"), T, d_model, dt, float(eps), float(rope_base), _ptr(th),
+        _dev(kv_cache, "kv_cache"),
         int(kv_cache.shape[0]), int(kv_cache.shape[1]), _dev(block_table, "block_table", torch.int32),
         int(block_table.shape[0]), int(block_table.shape[1]), _dev(seq_idx, "seq_idx", torch.int32),
         _dev(pos, "pos", torch.int32), _dev(workspace, "workspace"), int(workspace.numel()),
@@ -437,7 +469,7 @@ def mla_prefill_mha_workspace(max_seq_len, n_h):
 
 
 def mla_prefill_mha(q_nope, q_rope, q_pos, w_uk, w_uv, kv_cache, block_table, seq_lens, q_len,
-                    softmax_scale, rope_base, out, lse, workspace, stream=None):
+                    softmax_scale, rope_base, out, lse, workspace, stream=None, rope_theta=None):
     """Non-absorbed chunked prefill (see mla.h).  seq_lens is a host array [B]."""
     import numpy as np
     torch = _torch()
@@ -460,13 +492,14 @@ def mla_prefill_mha(q_nope, q_rope, q_pos, w_uk, w_uv, kv_cache, block_table, se
     if workspace.dtype != torch.uint8:
         raise TypeError("workspace must be a uint8 tensor")
     f32 = torch.float32
+    th = _theta(rope_theta)
     st = load().mla_prefill_mha(
         _dev(q_nope, "q_nope"), _dev(q_rope, "q_rope"), _dev(q_pos, "q_pos", torch.int32),
         _dev(w_uk, "w_uk"), _dev(w_uv, "w_uv"), _dev(kv_cache, "kv_cache"),
         int(kv_cache.shape[0]), int(kv_cache.shape[1]),
         _dev(block_table, "block_table", torch.int32), int(block_table.shape[1]),
         lens.ctypes.data_as(ctypes.c_void_p), B, int(q_len), n_h, dt, float(softmax_scale),
-        float(rope_base), _dev(out, "out", f32), _dev(lse, "lse", f32),
+        float(rope_base), _ptr(th), _dev(out, "out", f32), _dev(lse, "lse", f32),
         _dev(workspace, "workspace"), int(workspace.numel()), _stream(stream))
     _check("mla_prefill_mha", st)
 

@@ -29,8 +29,8 @@ namespace {
 
 constexpr int CCH = 64;        // latent columns per workgroup
 
-// RoPE frequencies in revolutions per position, theta_k / (2 pi) with
-// theta_k = base^(-2k / d_R), computed on the host in float64.
+// RoPE frequencies in revolutions per position, theta_k / (2 pi), computed
+// on the host in float64 from the pair frequencies theta_k.
 struct RopeRev {
   double r[D_R / 2];
 };
@@ -97,7 +97,7 @@ template <class E>
 __global__ void __launch_bounds__(256) absorb_q_kernel(
     const typename E::storage* __restrict__ q_nope, const typename E::storage* __restrict__ q_rope,
     const typename E::storage* __restrict__ w_uk, const int* __restrict__ q_pos, int T, int n_h,
-    double base, RopeRev rev, typename E::storage* __restrict__ q_lat) {
+    RopeFreq rf, RopeRev rev, typename E::storage* __restrict__ q_lat) {
   using T_ = typename E::storage;
   constexpr int S = AbsorbLds<E>::stride;
   __shared__ __attribute__((aligned(16))) char lds[D_H * S];
@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
       const T_* src = q_rope + ((long)t * n_h + h) * D_R;
       T_* dst = q_lat + ((long)t * n_h + h) * ROW + D_C;
       double c, s;
-      rope_cs(q_pos[t], k, base, c, s);
+      rope_cs(q_pos[t], rf.theta[k], c, s);
       double x = E::to_f32(src[2 * k]), y = E::to_f32(src[2 * k + 1]);
       dst[2 * k] = E::from_f32((float)(x * c - y * s));
       dst[2 * k + 1] = E::from_f32((float)(x * s + y * c));
@@ -229,19 +229,19 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
 }  // namespace
 
 hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
-                           const int* q_pos, int T, int n_h, int dtype, float base, void* q_lat,
-                           hipStream_t stream) {
+                           const int* q_pos, int T, int n_h, int dtype, const RopeFreq& rf,
+                           void* q_lat, hipStream_t stream) {
   dim3 grid(n_h, D_C / CCH, (T + TCH - 1) / TCH), block(256);
   RopeRev rev;
   for (int k = 0; k < D_R / 2; ++k)
-    rev.r[k] = std::pow((double)base, -(double)(2 * k) / (double)D_R) / 6.283185307179586;
+    rev.r[k] = rf.theta[k] / 6.283185307179586;
   if (dtype == 1)
     hipLaunchKernelGGL(absorb_q_kernel<BF16>, grid, block, 0, stream, (const uint16_t*)q_nope,
                        (const uint16_t*)q_rope, (const uint16_t*)w_uk, q_pos, T, n_h,
-                       (double)base, rev, (uint16_t*)q_lat);
+                       rf, rev, (uint16_t*)q_lat);
   else
     hipLaunchKernelGGL(absorb_q_kernel<F32>, grid, block, 0, stream, (const float*)q_nope,
-                       (const float*)q_rope, (const float*)w_uk, q_pos, T, n_h, (double)base, rev,
+                       (const float*)q_rope, (const float*)w_uk, q_pos, T, n_h, rf, rev,
                        (float*)q_lat);
   return hipGetLastError();
 }

@@ -15,7 +15,7 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
     typename E::storage* __restrict__ cache, int num_blocks, const int* __restrict__ table,
     int num_seqs, int max_blocks, const typename E::storage* __restrict__ c_kv,
     const typename E::storage* __restrict__ k_rope, const int* __restrict__ seq_idx,
-    const int* __restrict__ pos, int n, double base) {
+    const int* __restrict__ pos, int n, RopeFreq rf) {
   using T = typename E::storage;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -36,7 +36,7 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
   // rotated RoPE key
   if (lane < D_R / 2) {
     double c, s;
-    rope_cs(p, lane, base, c, s);
+    rope_cs(p, rf.theta[lane], c, s);
     const T* kr = k_rope + (long)r * D_R;
     double x = E::to_f32(kr[2 * lane]), y = E::to_f32(kr[2 * lane + 1]);
     dst[D_C + 2 * lane] = E::from_f32((float)(x * c - y * s));
@@ -46,17 +46,17 @@ __global__ void __launch_bounds__(256) kv_append_kernel(
 
 hipError_t launch_kv_append(void* cache, int dtype, int num_blocks, const int* table,
                             int num_seqs, int max_blocks, const void* c_kv, const void* k_rope,
-                            const int* seq_idx, const int* pos, int n, float base,
+                            const int* seq_idx, const int* pos, int n, const RopeFreq& rf,
                             hipStream_t stream) {
   dim3 grid((n + 3) / 4), block(256);
   if (dtype == 1)
     hipLaunchKernelGGL(kv_append_kernel<BF16>, grid, block, 0, stream, (uint16_t*)cache,
                        num_blocks, table, num_seqs, max_blocks, (const uint16_t*)c_kv,
-                       (const uint16_t*)k_rope, seq_idx, pos, n, (double)base);
+                       (const uint16_t*)k_rope, seq_idx, pos, n, rf);
   else
     hipLaunchKernelGGL(kv_append_kernel<F32>, grid, block, 0, stream, (float*)cache,
                        num_blocks, table, num_seqs, max_blocks, (const float*)c_kv,
-                       (const float*)k_rope, seq_idx, pos, n, (double)base);
+                       (const float*)k_rope, seq_idx, pos, n, rf);
   return hipGetLastError();
 }
 

@@ -41,33 +41,56 @@ const char* mla_status_string(int32_t status) {
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
 
+int32_t mla_rope_theta(double base, double scale, double alpha, double beta, double orig_ctx,
+                       double* theta) {
+  if (!theta) return MLA_ERR_NULL;
+  if (!(base > 1.0) || !std::isfinite(base) || !(scale >= 1.0) || !std::isfinite(scale) ||
+      !(alpha >= 0.0) || !(beta > alpha) || !std::isfinite(beta) || !(orig_ctx > 0.0) ||
+      !std::isfinite(orig_ctx))
+    return MLA_ERR_SHAPE;
+  const double two_pi = 6.283185307179586;
+  for (int k = 0; k < 32; ++k) {
+    const double f = std::pow(base, -(double)(2 * k) / 64.0);
+    // turns the pair makes over the original window, and where that lies on
+    // the ramp from alpha (interpolate fully) to beta (keep as is)
+    const double turns = orig_ctx * f / two_pi;
+    const double keep = std::min(1.0, std::max(0.0, (turns - alpha) / (beta - alpha)));
+    theta[k] = keep * f + (1.0 - keep) * (f / scale);
+  }
+  return MLA_OK;
+}
+
 int32_t mla_kv_append(void* kv_cache, int32_t dtype, int32_t num_blocks, int32_t block_size,
                       const int32_t* block_table, int32_t num_seqs, int32_t max_blocks,
                       const void* c_kv, const void* k_rope, const int32_t* seq_idx,
-                      const int32_t* pos, int32_t n, float rope_base, void* stream) {
+                      const int32_t* pos, int32_t n, float rope_base, const double* rope_theta,
+                      void* stream) {
   if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  mla::RopeFreq rf;
   if (n < 0 || num_blocks < 1 || num_seqs < 1 || max_blocks < 1 || block_size != MLA_BLOCK ||
-      !(rope_base > 0.0f))
+      !mla::rope_freq(rope_base, rope_theta, rf))
     return MLA_ERR_SHAPE;
   if (n == 0) return MLA_OK;
   if (!kv_cache || !block_table || !c_kv || !k_rope || !seq_idx || !pos) return MLA_ERR_NULL;
   if (!aligned16(kv_cache) || !aligned16(c_kv) || !aligned4(k_rope)) return MLA_ERR_ALIGN;
   return hip_status(mla::launch_kv_append(kv_cache, dtype, num_blocks, block_table, num_seqs,
-                                          max_blocks, c_kv, k_rope, seq_idx, pos, n, rope_base,
+                                          max_blocks, c_kv, k_rope, seq_idx, pos, n, rf,
                                           (hipStream_t)stream));
 }
 
 int32_t mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
                      const int32_t* q_pos, int32_t T, int32_t n_h, int32_t dtype,
-                     float rope_base, void* q_lat, void* stream) {
+                     float rope_base, const double* rope_theta, void* q_lat, void* stream) {
   if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
-  if (T < 0 || n_h < 16 || n_h % 16 != 0 || !(rope_base > 0.0f)) return MLA_ERR_SHAPE;
+  mla::RopeFreq rf;
+  if (T < 0 || n_h < 16 || n_h % 16 != 0 || !mla::rope_freq(rope_base, rope_theta, rf))
+    return MLA_ERR_SHAPE;
   if (T == 0) return MLA_OK;
   if (!q_nope || !q_rope || !w_uk || !q_pos || !q_lat) return MLA_ERR_NULL;
   if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat) || !aligned4(q_rope))
     return MLA_ERR_ALIGN;
-  return hip_status(mla::launch_absorb_q(q_nope, q_rope, w_uk, q_pos, T, n_h, dtype, rope_base,
-                                         q_lat, (hipStream_t)stream));
+  return hip_status(mla::launch_absorb_q(q_nope, q_rope, w_uk, q_pos, T, n_h, dtype, rf, q_lat,
+                                         (hipStream_t)stream));
 }
 
 int32_t mla_decode_paged(const void* q_lat, const void* kv_cache, int32_t num_blocks,

@@ -151,12 +151,11 @@ __device__ __forceinline__ void tile_barrier() {
   __syncthreads();
 }
 
-// RoPE pair k at position pos: cos/sin of pos * base^(-2k/64), with the angle
-// formed and evaluated in float64 (fp32 angles lose ~1e-2 rad near 128K).
-__device__ __forceinline__ void rope_cs(int pos, int k, double base, double& c, double& s) {
-  double theta = pow(base, -(double)(2 * k) / (double)D_R);
-  double ang = (double)pos * theta;
-  sincos(ang, &s, &c);
+// RoPE pair at position pos with frequency theta (radians per position):
+// cos/sin of pos * theta, with the angle formed and evaluated in float64
+// (fp32 angles lose ~1e-2 rad near 128K).
+__device__ __forceinline__ void rope_cs(int pos, double theta, double& c, double& s) {
+  sincos((double)pos * theta, &s, &c);
 }
 
 // One unit of attention work: query row (b, m) against keys [kb, ke) of

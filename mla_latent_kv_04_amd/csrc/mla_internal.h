@@ -4,16 +4,35 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 namespace mla {
+
+// RoPE pair frequencies theta_k (radians per position) of the 64-wide
+// decoupled key, k = 0..31, passed by value to the kernels that rotate.
+struct RopeFreq {
+  double theta[32];
+};
+
+// Plain RoPE, theta_k = base^(-2k/64), when `theta` is null; otherwise a copy
+// of the caller's table (e.g. YaRN's).  False if base or an entry is not a
+// finite positive number.
+inline bool rope_freq(float base, const double* theta, RopeFreq& rf) {
+  for (int k = 0; k < 32; ++k) {
+    rf.theta[k] = theta ? theta[k] : std::pow((double)base, -(double)(2 * k) / 64.0);
+    if (!(std::isfinite(rf.theta[k]) && rf.theta[k] > 0.0)) return false;
+  }
+  return true;
+}
 
 hipError_t launch_kv_append(void* cache, int dtype, int num_blocks, const int* table,
                             int num_seqs, int max_blocks, const void* c_kv, const void* k_rope,
-                            const int* seq_idx, const int* pos, int n, float base,
+                            const int* seq_idx, const int* pos, int n, const RopeFreq& rf,
                             hipStream_t stream);
 
 hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
-                           const int* q_pos, int T, int n_h, int dtype, float base, void* q_lat,
-                           hipStream_t stream);
+                           const int* q_pos, int T, int n_h, int dtype, const RopeFreq& rf,
+                           void* q_lat, hipStream_t stream);
 
 // Paged attention.  Uniform splits when work == nullptr (S splits per row,
 // partials at row (b * S + s) * q_len + m when S > 1), else a work list of
@@ -56,7 +75,7 @@ long kv_produce_workspace(int T, int d_model);
 long q_produce_workspace(int T, int d_model, int d_cq, int dtype);
 hipError_t launch_kv_produce(const void* h, const void* w_dkv, const float* kv_gain,
                              const void* w_kr, int T, int d_model, int dtype, float eps,
-                             float base, void* cache, int num_blocks, const int* table,
+                             const RopeFreq& rf, void* cache, int num_blocks, const int* table,
                              int num_seqs, int max_blocks, const int* seq_idx, const int* pos,
                              void* workspace, hipStream_t stream);
 hipError_t launch_q_produce(const void* h, const void* w_dq, const float* q_gain,
@@ -80,7 +99,7 @@ hipError_t launch_prefill_mha(const void* q_nope, const void* q_rope, const int*
                               const void* w_uk, const void* w_uv, const void* cache,
                               int num_blocks, const int* table, int max_blocks,
                               const int* seq_lens, int B, int q_len, int n_h, float scale,
-                              float base, float* out, float* lse, void* workspace,
+                              const RopeFreq& rf, float* out, float* lse, void* workspace,
                               hipStream_t stream);
 
 }  // namespace mla

@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
     const int* __restrict__ q_pos, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vt, const uint16_t* __restrict__ cache, int num_blocks,
     const int* __restrict__ trow, int L, int q_len, int Lpad, int n_h, int row0,
-    float scale_log2, double base, float* __restrict__ out, float* __restrict__ lse) {
+    float scale_log2, RopeFreq rf, float* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         double cs, sn;
-        rope_cs(pos, 16 * (ks - 4) + 4 * g + u, base, cs, sn);
+        rope_cs(pos, rf.theta[16 * (ks - 4) + 4 * g + u], cs, sn);
         const double x = bf16_to_f32((uint16_t)raw[2 * u]), y = bf16_to_f32((uint16_t)raw[2 * u + 1]);
         rot[2 * u] = (short)f32_to_bf16((float)(x * cs - y * sn));
         rot[2 * u + 1] = (short)f32_to_bf16((float)(x * sn + y * cs));
@@ -282,7 +282,7 @@ hipError_t launch_prefill_mha(const void* q_nope, const void* q_rope, const int*
                               const void* w_uk, const void* w_uv, const void* cache,
                               int num_blocks, const int* table, int max_blocks,
                               const int* seq_lens, int B, int q_len, int n_h, float scale,
-                              float base, float* out, float* lse, void* workspace,
+                              const RopeFreq& rf, float* out, float* lse, void* workspace,
                               hipStream_t stream) {
   const auto* cache16 = static_cast<const uint16_t*>(cache);
   for (int b = 0; b < B; ++b) {
@@ -310,7 +310,7 @@ hipError_t launch_prefill_mha(const void* q_nope, const void* q_rope, const int*
                        stream,
                        static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope),
                        q_pos, kc, vt, cache16, num_blocks, trow, L, q_len, lpad, n_h, b * q_len,
-                       scale * 1.4426950408889634f, (double)base, out, lse);
+                       scale * 1.4426950408889634f, rf, out, lse);
   }
   return hipGetLastError();
 }

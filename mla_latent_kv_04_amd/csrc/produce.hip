@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(256) kv_epilogue_kernel(
     const float* __restrict__ part, int S, int T, const float* __restrict__ gain, float eps,
     typename E::storage* __restrict__ cache, int num_blocks, const int* __restrict__ table,
     int num_seqs, int max_blocks, const int* __restrict__ seq_idx, const int* __restrict__ pos,
-    double base) {
+    RopeFreq rf) {
   using Ts = typename E::storage;
   __shared__ float red[4][ROW];
   const int r = blockIdx.x;
@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(256) kv_epilogue_kernel(
   }
   if (lane < D_R / 2) {
     double cs, sn;
-    rope_cs(p, lane, base, cs, sn);
+    rope_cs(p, rf.theta[lane], cs, sn);
     const double x = kx, yv = ky;
     dst[D_C + 2 * lane] = E::from_f32((float)(x * cs - yv * sn));
     dst[D_C + 2 * lane + 1] = E::from_f32((float)(x * sn + yv * cs));
@@ -276,7 +276,7 @@ void gemm_f32(const void* X, const void* W, int T, int N, int K, int kc, bool di
 
 template <class E>
 hipError_t kv_produce(const void* h, const void* w_dkv, const float* kv_gain, const void* w_kr,
-                      int T, int d_model, float eps, float base, void* cache, int num_blocks,
+                      int T, int d_model, float eps, const RopeFreq& rf, void* cache, int num_blocks,
                       const int* table, int num_seqs, int max_blocks, const int* seq_idx,
                       const int* pos, void* workspace, hipStream_t stream) {
   float* part = static_cast<float*>(workspace);
@@ -295,7 +295,7 @@ hipError_t kv_produce(const void* h, const void* w_dkv, const float* kv_gain, co
   }
   hipLaunchKernelGGL(kv_epilogue_kernel<E>, dim3(T), dim3(256), 0, stream, part, S, T, kv_gain,
                      eps, (typename E::storage*)cache, num_blocks, table, num_seqs, max_blocks,
-                     seq_idx, pos, (double)base);
+                     seq_idx, pos, rf);
   return hipGetLastError();
 }
 
@@ -467,13 +467,13 @@ long q_produce_workspace(int T, int d_model, int d_cq, int dtype) {
 
 hipError_t launch_kv_produce(const void* h, const void* w_dkv, const float* kv_gain,
                              const void* w_kr, int T, int d_model, int dtype, float eps,
-                             float base, void* cache, int num_blocks, const int* table,
+                             const RopeFreq& rf, void* cache, int num_blocks, const int* table,
                              int num_seqs, int max_blocks, const int* seq_idx, const int* pos,
                              void* workspace, hipStream_t stream) {
   if (dtype == 1)
-    return kv_produce<BF16>(h, w_dkv, kv_gain, w_kr, T, d_model, eps, base, cache, num_blocks,
+    return kv_produce<BF16>(h, w_dkv, kv_gain, w_kr, T, d_model, eps, rf, cache, num_blocks,
                             table, num_seqs, max_blocks, seq_idx, pos, workspace, stream);
-  return kv_produce<F32>(h, w_dkv, kv_gain, w_kr, T, d_model, eps, base, cache, num_blocks,
+  return kv_produce<F32>(h, w_dkv, kv_gain, w_kr, T, d_model, eps, rf, cache, num_blocks,
                          table, num_seqs, max_blocks, seq_idx, pos, workspace, stream);
 }
 

@@ -31,12 +31,14 @@ int64_t mla_kv_produce_workspace(int32_t T, int32_t d_model) {
 
 int32_t mla_kv_produce(const void* h, const void* w_dkv, const float* kv_gain, const void* w_kr,
                        int32_t T, int32_t d_model, int32_t dtype, float eps, float rope_base,
-                       void* kv_cache, int32_t num_blocks, int32_t block_size,
+                       const double* rope_theta, void* kv_cache, int32_t num_blocks, int32_t block_size,
                        const int32_t* block_table, int32_t num_seqs, int32_t max_blocks,
                        const int32_t* seq_idx, const int32_t* pos, void* workspace,
                        int64_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
-  if (T < 0 || d_model < 64 || d_model % 64 != 0 || !(eps >= 0.0f) || !(rope_base > 0.0f) ||
+  mla::RopeFreq rf;
+  if (T < 0 || d_model < 64 || d_model % 64 != 0 || !(eps >= 0.0f) ||
+      !mla::rope_freq(rope_base, rope_theta, rf) ||
       num_blocks < 1 || block_size != MLA_BLOCK || num_seqs < 1 || max_blocks < 1)
     return MLA_ERR_SHAPE;
   if (T == 0) return MLA_OK;
@@ -49,7 +51,7 @@ int32_t mla_kv_produce(const void* h, const void* w_dkv, const float* kv_gain, c
       !aligned16(workspace) || !aligned4(kv_gain))
     return MLA_ERR_ALIGN;
   return hip_status(mla::launch_kv_produce(h, w_dkv, kv_gain, w_kr, T, d_model, dtype, eps,
-                                           rope_base, kv_cache, num_blocks, block_table,
+                                           rf, kv_cache, num_blocks, block_table,
                                            num_seqs, max_blocks, seq_idx, pos, workspace,
                                            (hipStream_t)stream));
 }
@@ -133,11 +135,13 @@ int32_t mla_prefill_mha(const void* q_nope, const void* q_rope, const int32_t* q
                         const void* w_uk, const void* w_uv, const void* kv_cache,
                         int32_t num_blocks, int32_t block_size, const int32_t* block_table,
                         int32_t max_blocks, const int32_t* seq_lens, int32_t B, int32_t q_len,
-                        int32_t n_h, int32_t dtype, float scale, float rope_base, float* out,
-                        float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+                        int32_t n_h, int32_t dtype, float scale, float rope_base,
+                        const double* rope_theta, float* out, float* lse, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
   if (dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  mla::RopeFreq rf;
   if (B < 0 || q_len < 0 || n_h < 1 || n_h > 1024 || block_size != MLA_BLOCK || max_blocks < 1 ||
-      num_blocks < 1 || !(scale > 0.0f) || !(rope_base > 0.0f))
+      num_blocks < 1 || !(scale > 0.0f) || !mla::rope_freq(rope_base, rope_theta, rf))
     return MLA_ERR_SHAPE;
   if (B == 0 || q_len == 0) return MLA_OK;
   if (!seq_lens) return MLA_ERR_NULL;
@@ -160,7 +164,7 @@ int32_t mla_prefill_mha(const void* q_nope, const void* q_rope, const int32_t* q
     return MLA_ERR_ALIGN;
   return hip_status(mla::launch_prefill_mha(q_nope, q_rope, q_pos, w_uk, w_uv, kv_cache,
                                             num_blocks, block_table, max_blocks, seq_lens, B,
-                                            q_len, n_h, scale, rope_base, out, lse, workspace,
+                                            q_len, n_h, scale, rf, out, lse, workspace,
                                             (hipStream_t)stream));
 }
 

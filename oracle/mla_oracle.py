@@ -307,7 +307,7 @@ def rms_norm(x, gain, eps: float):
     return np.asarray(gain, F64) * x / np.sqrt(ms + float(eps))
 
 
-def kv_produce(h, w_dkv, kv_gain, w_kr, pos, base: float, eps: float):
+def kv_produce(h, w_dkv, kv_gain, w_kr, pos, base: float, eps: float, theta=None):
     """Cache rows of new tokens from their hidden states h [T, d_model].
 
     c^KV_t = RMSNorm(W^DKV h_t)          (notes §2.1.2 eq. 9, blog §3.1.1; R8)
@@ -318,7 +318,7 @@ def kv_produce(h, w_dkv, kv_gain, w_kr, pos, base: float, eps: float):
     h = np.asarray(h, F64)
     c_kv = rms_norm(h @ np.asarray(w_dkv, F64).T, kv_gain, eps)
     k_r = h @ np.asarray(w_kr, F64).T
-    return c_kv, k_r, kv_cache_rows(c_kv, k_r, pos, base)
+    return c_kv, k_r, kv_cache_rows(c_kv, k_r, pos, base, theta)
 
 
 def q_produce(h, w_dq, q_gain, w_uq, w_qr, n_h: int, eps: float):

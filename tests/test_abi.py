@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 2
+    assert lib.mla_abi_version() == 3
     for s in range(7):
         assert len(B.status_string(s)) > 0
     assert "scratch" in B.status_string(6)
@@ -100,17 +100,33 @@ def test_noalloc_refuses_sizes_beyond_its_scratch_without_a_gpu(lib):
                                         2, NULL, FAKE, None) == 1
 
 
+def _table(*bad):
+    th = np.full(32, 0.5)
+    for k, v in bad:
+        th[k] = v
+    return th, th.ctypes.data_as(ctypes.c_void_p)
+
+
 def test_other_entry_points_reject_bad_arguments(lib):
-    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, FAKE, 4, 24, 1, 1e4, FAKE, None) == 2
-    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, NULL, 4, 16, 1, 1e4, FAKE, None) == 1
-    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, FAKE, 4, 16, 2, 1e4, FAKE, None) == 4
-    assert lib.mla_absorb_q(FAKE, FAKE, MISALIGNED, FAKE, 4, 16, 1, 1e4, FAKE, None) == 3
-    assert lib.mla_absorb_q(NULL, NULL, NULL, NULL, 0, 16, 1, 1e4, NULL, None) == 0
-    assert lib.mla_kv_append(FAKE, 1, 4, 64, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 0.0, None) == 2
-    assert lib.mla_kv_append(FAKE, 1, 4, 64, NULL, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 1e4, None) == 1
-    assert lib.mla_kv_append(FAKE, 1, 4, 16, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 1e4, None) == 2
-    assert lib.mla_kv_append(MISALIGNED, 1, 4, 64, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 1e4,
-                             None) == 3
+    good, GOOD = _table()
+    _, ZERO = _table((31, 0.0))
+    _, NAN = _table((3, float("nan")))
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, FAKE, 4, 24, 1, 1e4, NULL, FAKE, None) == 2
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, NULL, 4, 16, 1, 1e4, NULL, FAKE, None) == 1
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, FAKE, 4, 16, 2, 1e4, NULL, FAKE, None) == 4
+    assert lib.mla_absorb_q(FAKE, FAKE, MISALIGNED, FAKE, 4, 16, 1, 1e4, NULL, FAKE, None) == 3
+    assert lib.mla_absorb_q(NULL, NULL, NULL, NULL, 0, 16, 1, 1e4, NULL, NULL, None) == 0
+    # a table replaces the base (a bad base is then unused); a bad entry is refused
+    assert lib.mla_absorb_q(NULL, NULL, NULL, NULL, 0, 16, 1, 0.0, GOOD, NULL, None) == 0
+    assert lib.mla_absorb_q(NULL, NULL, NULL, NULL, 0, 16, 1, 1e4, ZERO, NULL, None) == 2
+    assert lib.mla_absorb_q(NULL, NULL, NULL, NULL, 0, 16, 1, 1e4, NAN, NULL, None) == 2
+    ap = lib.mla_kv_append
+    assert ap(FAKE, 1, 4, 64, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 0.0, NULL, None) == 2
+    assert ap(FAKE, 1, 4, 64, NULL, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 1e4, NULL, None) == 1
+    assert ap(FAKE, 1, 4, 16, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 1e4, NULL, None) == 2
+    assert ap(MISALIGNED, 1, 4, 64, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 1e4, NULL, None) == 3
+    assert ap(FAKE, 1, 4, 64, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 3, 1e4, ZERO, None) == 2
+    assert ap(FAKE, 1, 4, 64, FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, 0, 0.0, GOOD, None) == 0
     assert lib.mla_splitkv_combine(FAKE, FAKE, 2, 0, 1, 16, FAKE, FAKE, None) == 2
     assert lib.mla_splitkv_combine(FAKE, NULL, 2, 2, 1, 16, FAKE, FAKE, None) == 1
     assert lib.mla_out_proj(FAKE, FAKE, 4, 16, 3, FAKE, None) == 4
@@ -125,6 +141,30 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert op(FAKE, FAKE, FAKE, FAKE, 2, FAKE, 4, 16, 1, MISALIGNED, FAKE, None) == 3
     assert op(FAKE, MISALIGNED, FAKE, FAKE, 2, FAKE, 4, 16, 1, FAKE, FAKE, None) == 3
     assert op(NULL, NULL, NULL, NULL, 0, NULL, 0, 16, 1, NULL, NULL, None) == 0  # T == 0
+
+
+def test_rope_theta_matches_the_oracle():
+    """The library's host YaRN table against the oracle's (same float64
+    formula, different code): equal to a few ulp, for DeepSeek-V2's setting and
+    for settings that move every pair through the ramp."""
+    for base, s, a, b, L0 in [(1e4, 40, 1, 32, 4096), (1e4, 1, 1, 32, 4096),
+                              (5e5, 8, 0.5, 64, 8192), (1e4, 40, 0, 1e6, 4096)]:
+        got = pkg.mla_rope_theta(base, s, a, b, L0)
+        want = orc.yarn_theta(64, base, s, a, b, L0)
+        np.testing.assert_allclose(got, want, rtol=4e-16, atol=0)
+
+
+def test_rope_theta_rejects_bad_settings(lib):
+    out = np.zeros(32)
+    P = out.ctypes.data_as(ctypes.c_void_p)
+    assert lib.mla_rope_theta(1e4, 40, 1, 32, 4096, NULL) == 1
+    for args in [(1.0, 40, 1, 32, 4096), (1e4, 0.5, 1, 32, 4096), (1e4, 40, 32, 32, 4096),
+                 (1e4, 40, -1, 32, 4096), (1e4, 40, 1, 32, 0), (float("nan"), 40, 1, 32, 4096),
+                 (1e4, float("inf"), 1, 32, 4096)]:
+        assert lib.mla_rope_theta(*args, P) == 2, args
+    assert lib.mla_rope_theta(1e4, 40, 1, 32, 4096, P) == 0
+    with pytest.raises(ValueError):
+        B._theta(np.ones(31))
 
 
 def test_split_plan_matches_oracle_rule():
@@ -151,14 +191,16 @@ def test_producers_reject_bad_arguments_and_size_their_workspace(lib):
     need = ws(4, 64)
 
     def kv(**kw):
-        a = dict(h=FAKE, wd=FAKE, g=FAKE, wk=FAKE, T=4, dm=64, dt=1, eps=1e-6, base=1e4, kv=FAKE,
-                 nb=4, bs=64, tab=FAKE, ns=1, mb=4, seq=FAKE, pos=FAKE, w=FAKE, wb=need)
+        a = dict(h=FAKE, wd=FAKE, g=FAKE, wk=FAKE, T=4, dm=64, dt=1, eps=1e-6, base=1e4, th=NULL,
+                 kv=FAKE, nb=4, bs=64, tab=FAKE, ns=1, mb=4, seq=FAKE, pos=FAKE, w=FAKE, wb=need)
         a.update(kw)
         return lib.mla_kv_produce(a["h"], a["wd"], a["g"], a["wk"], a["T"], a["dm"], a["dt"],
-                                  a["eps"], a["base"], a["kv"], a["nb"], a["bs"], a["tab"],
+                                  a["eps"], a["base"], a["th"], a["kv"], a["nb"], a["bs"], a["tab"],
                                   a["ns"], a["mb"], a["seq"], a["pos"], a["w"], a["wb"], None)
     assert kv(dt=3) == 4
     assert kv(dm=48) == 2 and kv(dm=96) == 2 and kv(bs=32) == 2 and kv(eps=-1.0) == 2 and kv(base=0.0) == 2
+    _, NEG = _table((0, -1.0))
+    assert kv(th=NEG) == 2
     assert kv(wb=need - 1) == 2                      # workspace too small
     assert kv(h=NULL) == 1 and kv(w=NULL) == 1
     assert kv(kv=MISALIGNED) == 3
@@ -195,13 +237,15 @@ def test_prefill_mha_rejects_bad_arguments_and_sizes_its_workspace(lib):
     def pf(**kw):
         a = dict(qn=FAKE, qr=FAKE, qp=FAKE, wk=FAKE, wv=FAKE, kv=FAKE, nb=16, bs=64, tab=FAKE,
                  mb=8, lens=lens.ctypes.data, B=2, q=100, nh=16, dt=1, sc=0.07, base=1e4,
-                 out=FAKE, lse=FAKE, w=FAKE, wb=need)
+                 th=NULL, out=FAKE, lse=FAKE, w=FAKE, wb=need)
         a.update(kw)
         return lib.mla_prefill_mha(a["qn"], a["qr"], a["qp"], a["wk"], a["wv"], a["kv"], a["nb"],
                                    a["bs"], a["tab"], a["mb"], a["lens"], a["B"], a["q"], a["nh"],
-                                   a["dt"], a["sc"], a["base"], a["out"], a["lse"], a["w"],
+                                   a["dt"], a["sc"], a["base"], a["th"], a["out"], a["lse"], a["w"],
                                    a["wb"], None)
     assert pf(dt=0) == 4                                  # bf16 only
+    _, INF = _table((7, float("inf")))
+    assert pf(th=INF) == 2
     assert pf(bs=32) == 2 and pf(nh=0) == 2 and pf(sc=0.0) == 2 and pf(base=-1.0) == 2
     assert pf(mb=4) == 2                                  # 300 keys need 5 blocks of 64
     assert pf(wb=need - 1) == 2
