@@ -23,7 +23,7 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Widths are fixed by the pages for both DeepSeek-V2 and V2-Lite: d_c = 512,
- *   d_R = 64, d_h = 128 (blog part 2 §3.1.1 and the V2-Lite description).
+ *   d_R = 64, d_h = 128 (blog part 3 §3.1.1 and the V2-Lite description in part 2).
  * - dtype: MLA_F32 (IEEE float) or MLA_BF16 (bfloat16 as raw 16-bit words).
  *   Arithmetic is fp32 in both cases (products of bf16 operands are exact in
  *   fp32; sums accumulate in fp32).  o_lat, lse, partials and the output are
@@ -98,7 +98,7 @@ int32_t mla_abi_version(void);
  *
  * DeepSeek-V2 extends its 4K context to 128K by applying YaRN to the
  * decoupled shared key only, with scale s = 40, ramp bounds alpha = 1 and
- * beta = 32, aiming at 160K = 40 x 4K (DeepSeek-V2 MLA blog, part 2 §3.1.3).
+ * beta = 32, aiming at 160K = 40 x 4K (DeepSeek-V2 MLA blog, part 3 §3.1.3).
  * Read as YaRN's by-parts rule: pair k of plain RoPE, f_k = base^(-2k/64),
  * makes r_k = orig_ctx * f_k / (2 pi) turns over the original window; with
  * g_k = clamp((r_k - alpha) / (beta - alpha), 0, 1),
@@ -323,7 +323,7 @@ int32_t mla_out_proj_planned(float* o_lat, const float* o_part, const float* lse
 /*
  * Producers: the projections that feed the path from a layer's hidden states
  * h [T, d_model] (notes §2.1.2 eq. 9 and 12-13; blog part 2 §2.2.2 for the
- * decoupled key and query, §3.1.1 for the RMSNorm after the compressed
+ * decoupled key and query, part 3 §3.1.1 for the RMSNorm after the compressed
  * latents).  The RMSNorm is the standard one over the latent's width:
  *   RMSNorm(x) = g * x / sqrt(mean(x^2) + eps), g a learned gain (fp32).
  * Weights are stored as the equations write them, [d_out, d_in] row-major,

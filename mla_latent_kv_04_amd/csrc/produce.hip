@@ -6,7 +6,7 @@
 //   q^R  = W^QR c^Q                                 §2.1.2, eq. 12-13; the decoupled
 //                                                   key / query of the DeepSeek-V2 MLA
 //                                                   blog, adg.csdn.net, part 2 §2.2.2;
-//                                                   the latent RMSNorm of its §3.1.1)
+//                                                   the latent RMSNorm of its part 3 §3.1.1)
 //
 // Every projection is Y = X W^T with both operands' reduced axis contiguous
 // (X [T, K] rows, W [N, K] rows as eq. 9 writes them).  For decode sizes the

@@ -7,7 +7,7 @@ what it returns, so the two sides always see the same values.
 
 Shapes follow the pages: DeepSeek-V2 uses 128 heads of width 128, a 512-wide
 KV latent and a 64-wide decoupled RoPE key; V2-Lite uses 16 heads with the same
-widths ([adg.csdn.net blog, §3.1.1 and the V2-Lite part]).
+widths ([adg.csdn.net blog, part 3 §3.1.1, and the V2-Lite description in part 2]).
 
 Recipe (one ``numpy.random.Generator(PCG64(seed))`` per workload, draws in
 this order):
@@ -231,7 +231,7 @@ def make_hidden(prob: Problem, d_model: int = D_MODEL_V2,
                 d_cq: Optional[int] = D_CQ_V2) -> HiddenInputs:
     """Hidden states for the step's T tokens and random producer weights of the
     DeepSeek-V2 widths (hidden 5120, query compression 1536: adg.csdn.net blog,
-    §3.1.1).
+    part 3 §3.1.1).
 
     Recipe (its own ``Generator(PCG64(seed + 7919))``, draws in this order):
     h ~ N(0, 1); W^DKV, W^KR, W^DQ ~ N(0, 1/d_model); W^UQ, W^QR ~ N(0, 1/d_cq);

@@ -29,7 +29,7 @@ Readings where the pages are silent or garbled:
   R6 a query row with no visible key yields o = 0 and lse = -inf.
   R7 W^UK / W^UV are stored [n_h, d_h, d_c]: head i owns rows i*d_h..(i+1)*d_h
      of eq. 10/11's matrices (eq. 4-6 ordering).
-  R8 the extra RMSNorm after the compressed latents (blog §3.1.1 names it and
+  R8 the extra RMSNorm after the compressed latents (blog part 3 §3.1.1 names it and
      gives no formula) is the standard one, g * x / sqrt(mean(x^2) + eps) over
      the latent's width, with a learned gain g; it is applied to c^KV before it
      is cached and to c^Q before its up-projections.
@@ -42,7 +42,7 @@ Readings where the pages are silent or garbled:
   R10 a model that does not compress its queries (V2-Lite: blog, the V2-Lite
      paragraph) projects both query parts straight from the hidden state,
      q^C = W^QC h (eq. 1's W^Q, per-head rows) and q^R = W^QR h.
-  R11 YaRN (blog §3.1.3: applied to the decoupled RoPE key, scale 40, the two
+  R11 YaRN (blog part 3 §3.1.3: applied to the decoupled RoPE key, scale 40, the two
      ramp parameters 1 and 32, target context 160K) is read as YaRN's
      interpolation by parts on the RoPE pair frequencies: with the original
      context L0 = 4096 (the blog extends a 4K window; 40 x 4096 = 163,840 is
@@ -310,7 +310,7 @@ def rms_norm(x, gain, eps: float):
 def kv_produce(h, w_dkv, kv_gain, w_kr, pos, base: float, eps: float, theta=None):
     """Cache rows of new tokens from their hidden states h [T, d_model].
 
-    c^KV_t = RMSNorm(W^DKV h_t)          (notes §2.1.2 eq. 9, blog §3.1.1; R8)
+    c^KV_t = RMSNorm(W^DKV h_t)          (notes §2.1.2 eq. 9, blog part 3 §3.1.1; R8)
     k^R_t  = W^KR h_t, rotated at pos_t  (blog §2.2.2; R9)
     Returns (c_kv [T, d_c], k_r [T, d_R] before rotation, rows [T, d_c + d_R]),
     rows being what kv_cache_rows caches for them.
@@ -324,7 +324,7 @@ def kv_produce(h, w_dkv, kv_gain, w_kr, pos, base: float, eps: float, theta=None
 def q_produce(h, w_dq, q_gain, w_uq, w_qr, n_h: int, eps: float):
     """Per-head queries of tokens h [T, d_model] through the compressed query.
 
-    c^Q_t = RMSNorm(W^DQ h_t)    (notes §2.1.2 eq. 12, blog §3.1.1; R8)
+    c^Q_t = RMSNorm(W^DQ h_t)    (notes §2.1.2 eq. 12, blog part 3 §3.1.1; R8)
     q^C_t = W^UQ c^Q_t           (eq. 13), split into heads of d_h
     q^R_t = W^QR c^Q_t           (blog §2.2.2; R9), before rotation
     Returns (c_q [T, d_c'], q_nope [T, n_h, d_h], q_rope [T, n_h, d_R]).
