@@ -55,13 +55,27 @@ Readings where the pages are silent or garbled:
      rotation together).  The blog's attention-entropy factor is not printed
      (its formula is missing from the page): it multiplies every score, so it
      is part of the softmax scale the caller passes, and it is 1 here.
+  R12 the quantised latent cache (blog part 3 §3.1.4: the served model's KV
+     cache is quantised to about 6 bits per element on average, scheme not
+     given) is read as OCP FP8 E4M3 per element (sign, 4 exponent bits with
+     bias 7, 3 mantissa bits; subnormals; largest finite value 448; no
+     infinities) with two float32 scales per cached token, one for the 512
+     latent elements and one for the 64 rotated RoPE elements.  The values to
+     quantise are the float32 row (c^KV as given, k^R rotated in float64 and
+     rounded to float32).  Per part: amax = max |x|, s = amax / 448 in float32
+     (s = 1 for an all-zero part), code = the E4M3 value nearest to the
+     float32 quotient x / s, ties to even, clamped to +-448; the cached value
+     stands for s * code.  Attention over the quantised cache is the same
+     attention over those dequantised rows.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = [
-    "rope_rotate", "rope_theta", "yarn_theta", "mla_attention_naive", "kv_cache_rows", "absorb_query",
+    "rope_rotate", "rope_theta", "yarn_theta", "mla_attention_naive",
+    "e4m3_value", "e4m3_round", "e4m3_code", "quantize_rows", "dequantize_rows",
+    "kv_cache_rows_fp8", "kv_cache_rows", "absorb_query",
     "latent_attention", "split_ranges", "combine_splits", "out_projection",
     "visible_keys", "rms_norm", "kv_produce", "q_produce",
     "q_produce_direct", "o_projection",
@@ -359,3 +373,88 @@ def o_projection(out, w_o):
     T = out.shape[0]
     return out.reshape(T, -1) @ np.asarray(w_o, F64).T
 
+
+# ------------------------------------------------------- quantised latent cache
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code):
+    """Value of OCP FP8 E4M3 bytes (R12): bit 7 sign, bits 6-3 exponent (bias
+    7), bits 2-0 mantissa; exponent 0 holds subnormals m/8 * 2^-6; exponent 15
+    with mantissa 7 is NaN (the format has no infinities)."""
+    code = np.asarray(code, dtype=np.int64)
+    sign = np.where(code & 0x80, -1.0, 1.0)
+    e = (code >> 3) & 0xF
+    m = (code & 0x7).astype(F64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e.astype(F64) - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_round(y):
+    """The E4M3 value nearest to y, ties to even, clamped to +-448 (R12).
+
+    In the binade [2^E, 2^(E+1)) the values are spaced 2^(E-3); below 2^-6
+    (subnormals) the spacing is 2^-9.  y / spacing is then 8 + mantissa (or
+    the subnormal mantissa), so rounding it half-to-even picks the even
+    mantissa on a tie."""
+    y = np.asarray(y, F64)
+    a = np.abs(y)
+    _, ex = np.frexp(a)                       # a = f 2^ex, f in [0.5, 1)
+    E = np.maximum(ex.astype(F64) - 1.0, -6.0)
+    q = 2.0 ** (E - 3.0)
+    r = np.minimum(np.rint(a / q) * q, E4M3_MAX)
+    return np.copysign(r, y)
+
+
+def e4m3_code(v):
+    """Byte of an exact E4M3 value v (the inverse of e4m3_value on finite values)."""
+    v = np.asarray(v, F64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    E = ex - 1
+    normal = a >= 2.0 ** -6
+    e_field = np.where(normal, E + 7, 0)
+    m_field = np.where(normal, (a / 2.0 ** E.astype(F64) - 1.0) * 8.0, a / 2.0 ** -9)
+    code = (np.signbit(v).astype(np.int64) << 7) | (e_field.astype(np.int64) << 3) \
+        | np.rint(m_field).astype(np.int64)
+    return code.astype(np.uint8)
+
+
+def quantize_rows(rows, d_c: int):
+    """Quantise float32 cache rows [N, d_c + d_R] (R12).
+
+    Returns codes uint8 [N, d_c + d_R] and scales float32 [N, 2] (latent part,
+    RoPE part)."""
+    rows = np.asarray(rows, dtype=np.float32)
+    codes = np.empty(rows.shape, dtype=np.uint8)
+    scales = np.empty((rows.shape[0], 2), dtype=np.float32)
+    for k, (lo, hi) in enumerate([(0, d_c), (d_c, rows.shape[1])]):
+        x = rows[:, lo:hi]
+        amax = np.max(np.abs(x), axis=1)
+        s = amax / np.float32(E4M3_MAX)                     # float32 division
+        s = np.where(amax > 0, s, np.float32(1.0)).astype(np.float32)
+        y = x / s[:, None]                                  # float32 division
+        codes[:, lo:hi] = e4m3_code(e4m3_round(y.astype(F64)))
+        scales[:, k] = s
+    return codes, scales
+
+
+def dequantize_rows(codes, scales, d_c: int):
+    """The rows the quantised cache stands for: s * code, float64 (exact)."""
+    v = e4m3_value(codes)
+    s = np.asarray(scales, F64)
+    out = v.copy()
+    out[:, :d_c] *= s[:, 0:1]
+    out[:, d_c:] *= s[:, 1:2]
+    return out
+
+
+def kv_cache_rows_fp8(c_kv, k_r, pos, base: float, theta=None):
+    """Quantised cache rows of tokens at positions pos (R3, R12): the float32
+    row [c^KV ; R_pos k^R] (rotation in float64, then rounded to float32),
+    quantised.  Returns (codes uint8 [L, d_c + d_R], scales float32 [L, 2])."""
+    c_kv = np.asarray(c_kv, F64)
+    rows = kv_cache_rows(c_kv, k_r, pos, base, theta).astype(np.float32)
+    return quantize_rows(rows, c_kv.shape[1])

@@ -542,3 +542,118 @@ def test_o_projection_matches_scalar_loops():
     pick = np.zeros((1, n_h * d_h))
     pick[0, 1 * d_h + 2] = 1.0                 # head 1, dimension 2
     np.testing.assert_array_equal(orc.o_projection(out, pick)[:, 0], out[:, 1, 2])
+
+
+# ------------------------------------------------------- quantised latent cache
+
+def _e4m3_table():
+    """Finite E4M3 values by brute force from the bit layout (sign, 4-bit
+    exponent with bias 7, 3-bit mantissa, subnormals at exponent 0, NaN at
+    S.1111.111), independent of the oracle's decoder."""
+    vals = {}
+    for code in range(256):
+        s, e, m = code >> 7, (code >> 3) & 15, code & 7
+        if e == 15 and m == 7:
+            continue
+        mag = (m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        vals[code] = -mag if s else mag
+    return vals
+
+
+def test_e4m3_decoder_matches_the_bit_layout():
+    table = _e4m3_table()
+    v = orc.e4m3_value(np.arange(256))
+    for code in range(256):
+        if code in table:
+            assert v[code] == table[code] and math.copysign(1, v[code]) == math.copysign(1, table[code])
+        else:
+            assert np.isnan(v[code])
+    # landmarks of the format: 1.0, the largest value, the smallest normal and subnormal
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x08] == 2.0 ** -6 and v[0x01] == 2.0 ** -9
+    assert len(table) == 254 and np.nanmax(v) == 448.0
+    finite = np.array(sorted(table))
+    np.testing.assert_array_equal(orc.e4m3_code(v[finite]), finite)
+
+
+def test_e4m3_round_is_nearest_with_ties_to_even():
+    table = _e4m3_table()
+    pos = sorted({v for c, v in table.items() if v >= 0 and not (v == 0 and c & 0x80)})
+    even = {v: (c & 1) == 0 for c, v in table.items() if c < 0x80}
+    rng = np.random.default_rng(50)
+    ys = list(rng.uniform(0, 460, 2000)) + list(2.0 ** rng.uniform(-12, 8.8, 2000))
+    ys += [(a + b) / 2 for a, b in zip(pos, pos[1:])]          # every midpoint
+    ys += [448.0, 455.9, 464.0, 470.0, 1e4]
+    for y in ys:
+        got = orc.e4m3_round(y)
+        if y >= 448.0:
+            assert got == 448.0                                 # clamped
+            continue
+        d = [abs(y - v) for v in pos]
+        best = min(d)
+        cands = [v for v, dv in zip(pos, d) if dv == best]
+        want = cands[0] if len(cands) == 1 else [v for v in cands if even[v]][0]
+        assert got == want, (y, got, want)
+        assert orc.e4m3_round(-y) == -want
+    # worked cases: a tie goes to the even mantissa
+    assert orc.e4m3_round(1.0625) == 1.0 and orc.e4m3_round(1.1875) == 1.25
+    assert orc.e4m3_round(2.0 ** -10) == 0.0 and orc.e4m3_round(1.5 * 2.0 ** -9) == 2.0 ** -8
+
+
+def _fp32_rows(rng, n, scale_c=1.0, scale_r=1.0):
+    rows = np.concatenate([scale_c * rng.standard_normal((n, 512)),
+                           scale_r * rng.standard_normal((n, 64))], axis=1)
+    return rows.astype(np.float32)
+
+
+def test_quantised_rows_error_bounds_and_scale():
+    rng = np.random.default_rng(51)
+    rows = _fp32_rows(rng, 64, 3.0, 0.01)
+    codes, scales = orc.quantize_rows(rows, 512)
+    deq = orc.dequantize_rows(codes, scales, 512)
+    x = rows.astype(np.float64)
+    for k, (lo, hi) in enumerate([(0, 512), (512, 576)]):
+        amax = np.abs(x[:, lo:hi]).max(axis=1)
+        s = scales[:, k].astype(np.float64)
+        assert np.all(np.abs(s * 448 / amax - 1) < 2 ** -23)     # s = amax / 448 (one rounding)
+        # the largest element lands on +-448
+        arg = np.abs(x[:, lo:hi]).argmax(axis=1)
+        assert np.all(np.abs(orc.e4m3_value(codes[np.arange(64), lo + arg])) == 448.0)
+        err = np.abs(deq[:, lo:hi] - x[:, lo:hi])
+        y = np.abs(x[:, lo:hi]) / s[:, None]
+        normal = y >= 2.0 ** -6
+        # half a spacing: 2^-4 of the value (normal range), 2^-10 s (subnormal),
+        # plus the float32 quotient's rounding
+        assert np.all(err[normal] <= (2.0 ** -4 * np.abs(x[:, lo:hi]) + 1e-6 * s[:, None])[normal])
+        assert np.all(err[~normal] <= (2.0 ** -10 + 1e-7) * np.broadcast_to(s[:, None], err.shape)[~normal])
+    # each part has its own scale: the RoPE part, 300x smaller, is as precise
+    rel = np.abs(deq - x) / np.abs(x).max(axis=1, keepdims=True)
+    assert rel[:, 512:].max() < 0.05
+
+
+def test_quantised_rows_special_cases():
+    rows = np.zeros((3, 576), np.float32)
+    rows[1, 7] = -2.5
+    rows[2, 600 - 30] = 1e-30                                  # one tiny RoPE element
+    codes, scales = orc.quantize_rows(rows, 512)
+    assert np.all(codes[0] == 0) and np.all(scales[0] == 1.0)
+    assert codes[1, 7] == 0xFE and scales[1, 0] == np.float32(2.5) / np.float32(448)
+    assert np.all(codes[1, 512:] == 0) and scales[1, 1] == 1.0
+    assert orc.e4m3_value(codes[2, 570]) == 448.0
+    # re-quantising the dequantised rows gives the same codes
+    rng = np.random.default_rng(52)
+    r = _fp32_rows(rng, 16)
+    c1, s1 = orc.quantize_rows(r, 512)
+    c2, s2 = orc.quantize_rows(orc.dequantize_rows(c1, s1, 512).astype(np.float32), 512)
+    np.testing.assert_array_equal(c1, c2)
+
+
+def test_fp8_cache_rows_quantise_the_rotated_row():
+    t = _tiny(seed=53, L=9, d_c=512, d_r=64)
+    codes, scales = orc.kv_cache_rows_fp8(t["c_kv"], t["k_r"], np.arange(9), 1e4)
+    rows = orc.kv_cache_rows(t["c_kv"], t["k_r"], np.arange(9), 1e4)
+    deq = orc.dequantize_rows(codes, scales, 512)
+    assert np.max(np.abs(deq - rows) / np.abs(rows).max(axis=1, keepdims=True)) < 2.0 ** -4
+    # the RoPE part is quantised after the rotation: rotating the dequantised
+    # unrotated key would differ
+    un, su = orc.quantize_rows(np.concatenate([t["c_kv"], t["k_r"]], 1).astype(np.float32), 512)
+    assert np.any(un[:, 512:] != codes[:, 512:])
