@@ -435,6 +435,59 @@ int32_t mla_prefill_mha(const void* q_nope, const void* q_rope, const int32_t* q
                         int64_t workspace_bytes, void* stream);
 
 /*
+ * Quantised latent cache (DeepSeek-V2 MLA blog, part 3 §3.1.4: the served
+ * model's KV cache is quantised, about 6 bits per element on average, scheme
+ * not given).  Here: OCP FP8 E4M3 per element (bias 7, subnormals, largest
+ * finite 448, no infinities; the gfx950 conversion format) with two float32
+ * scales per token, one for the 512 latent elements and one for the 64
+ * rotated RoPE elements.
+ *   kv_cache  device, uint8 [num_blocks, 64, 576] E4M3 codes, rows contiguous
+ *             (576 bytes = 36 x 16), 16-byte aligned
+ *   kv_scale  device, float32 [num_blocks, 64, 2] = {s_latent, s_rope} per
+ *             row, 16-byte aligned
+ * Row j stands for [s_latent * c ; s_rope * r], c and r its E4M3 values.
+ * 584 bytes per token against 1152 for bf16.
+ *
+ * mla_kv_append_fp8 - mla_kv_append into the quantised cache.  The float32
+ * row [c_kv ; R_pos k_rope] (rotation formed in float64, then rounded to
+ * float32) is quantised per part: amax = max |x|, s = amax / 448 (float32
+ * division; s = 1 when amax = 0), code = E4M3 nearest-even of the float32
+ * quotient x / s, clamped to +-448.  c_kv / k_rope are dtype (MLA_F32 or
+ * MLA_BF16); slot rule, skipping and RoPE table as in mla_kv_append.
+ */
+int32_t mla_kv_append_fp8(void* kv_cache, float* kv_scale, int32_t dtype, int32_t num_blocks,
+                          int32_t block_size, const int32_t* block_table, int32_t num_seqs,
+                          int32_t max_blocks, const void* c_kv, const void* k_rope,
+                          const int32_t* seq_idx, const int32_t* pos, int32_t n, float rope_base,
+                          const double* rope_theta, void* stream);
+
+/*
+ * mla_decode_paged_fp8 / mla_decode_paged_planned_fp8 - mla_decode_paged and
+ * mla_decode_paged_planned over the quantised cache: the attention of
+ * mla_decode_paged with row j replaced by its dequantised value.  q_lat is
+ * bf16 [B * q_len, n_h, 576]; outputs and partials as there.  Scores take
+ * s_latent and s_rope per token on the two parts of the product; the
+ * softmax weight of token j in the value sum is rounded to bf16 after
+ * multiplication by its s_latent (an MFMA operand), and the normaliser sums
+ * those same weights divided by s_latent, so the output is an exact
+ * weighted mean of the dequantised latents.  Head counts as in
+ * mla_decode_paged; one workgroup per work item (no lists).
+ */
+int32_t mla_decode_paged_fp8(const void* q_lat, const void* kv_cache, const float* kv_scale,
+                             int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+                             int32_t max_blocks, const int32_t* seq_lens, int32_t B,
+                             int32_t q_len, int32_t n_h, float softmax_scale, int32_t num_splits,
+                             float* o_part, float* lse_part, float* o_lat, float* lse,
+                             void* stream);
+int32_t mla_decode_paged_planned_fp8(const void* q_lat, const void* kv_cache,
+                                     const float* kv_scale, int32_t num_blocks,
+                                     int32_t block_size, const int32_t* block_table,
+                                     int32_t max_blocks, int32_t B, int32_t q_len, int32_t n_h,
+                                     float softmax_scale, const int32_t* work, int32_t n_work,
+                                     float* o_part, float* lse_part, int32_t n_parts,
+                                     float* o_lat, float* lse, void* stream);
+
+/*
  * mla_decode_paged_noalloc - for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): mla_decode_paged followed, when num_splits > 1, by

@@ -24,7 +24,8 @@ _EXPORTS = ("mla_status_string", "mla_abi_version", "mla_rope_theta", "mla_kv_ap
             "mla_out_proj_planned", "mla_kv_produce_workspace", "mla_kv_produce",
             "mla_q_produce_workspace", "mla_q_produce", "mla_q_produce_direct",
             "mla_o_proj_workspace", "mla_o_proj",
-            "mla_prefill_mha_workspace", "mla_prefill_mha", "mla_decode_paged_noalloc")
+            "mla_prefill_mha_workspace", "mla_prefill_mha", "mla_kv_append_fp8",
+            "mla_decode_paged_fp8", "mla_decode_paged_planned_fp8", "mla_decode_paged_noalloc")
 
 
 class MLAError(RuntimeError):
@@ -80,6 +81,12 @@ def load() -> ctypes.CDLL:
         "mla_o_proj_workspace": (ctypes.c_int64, [_I, _I, _I, _I]),
         "mla_o_proj": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_int64, _P]),
         "mla_prefill_mha_workspace": (ctypes.c_int64, [_I, _I]),
+        "mla_kv_append_fp8": (_I, [_P, _P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I, _F, _P,
+                                   _P]),
+        "mla_decode_paged_fp8": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P,
+                                      _P, _P, _P]),
+        "mla_decode_paged_planned_fp8": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _F, _P, _I,
+                                              _P, _P, _I, _P, _P, _P]),
         "mla_decode_paged_noalloc": (_I, [_P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F, _I,
                                           _P, _P, _P]),
         "mla_prefill_mha": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F,
@@ -578,3 +585,97 @@ def mla_decode_paged_noalloc(q_lat, kv_cache, block_table, seq_lens, q_len, soft
         dt, float(softmax_scale), int(num_splits), _dev(o_lat, "o_lat", f32),
         _dev(lse, "lse", f32), _stream(stream))
     _check("mla_decode_paged_noalloc", st)
+
+
+# ---------------------------------------------------------------------------
+# Quantised (FP8 E4M3) latent cache
+# ---------------------------------------------------------------------------
+
+def _fp8_cache(kv_cache, kv_scale):
+    torch = _torch()
+    if kv_cache.dtype != torch.uint8 or kv_cache.dim() != 3 or kv_cache.shape[2] != ROW:
+        raise ValueError("an FP8 kv_cache is uint8 [num_blocks, 64, 576]")
+    if kv_scale.dtype != torch.float32 or tuple(kv_scale.shape) != (kv_cache.shape[0],
+                                                                    kv_cache.shape[1], 2):
+        raise ValueError("kv_scale must be float32 [num_blocks, 64, 2]")
+
+
+def mla_kv_append_fp8(kv_cache, kv_scale, block_table, c_kv, k_rope, seq_idx, pos,
+                      rope_base=10000.0, stream=None, rope_theta=None):
+    """Quantise rows [c_kv ; R_pos k_rope] into the FP8 cache (see mla.h)."""
+    torch = _torch()
+    _fp8_cache(kv_cache, kv_scale)
+    dt = _dtype_code(c_kv)
+    n = int(c_kv.shape[0])
+    if tuple(c_kv.shape) != (n, D_C) or tuple(k_rope.shape) != (n, D_R) or k_rope.dtype != c_kv.dtype:
+        raise ValueError("c_kv must be [n, 512] and k_rope [n, 64], of one dtype")
+    if tuple(seq_idx.shape) != (n,) or tuple(pos.shape) != (n,):
+        raise ValueError("seq_idx and pos must be [n]")
+    th = _theta(rope_theta)
+    st = load().mla_kv_append_fp8(
+        _dev(kv_cache, "kv_cache"), _dev(kv_scale, "kv_scale"), dt, int(kv_cache.shape[0]),
+        int(kv_cache.shape[1]), _dev(block_table, "block_table", torch.int32),
+        int(block_table.shape[0]), int(block_table.shape[1]), _dev(c_kv, "c_kv"),
+        _dev(k_rope, "k_rope"), _dev(seq_idx, "seq_idx", torch.int32),
+        _dev(pos, "pos", torch.int32), n, float(rope_base), _ptr(th), _stream(stream))
+    _check("mla_kv_append_fp8", st)
+
+
+def mla_decode_paged_fp8(q_lat, kv_cache, kv_scale, block_table, seq_lens, q_len, softmax_scale,
+                         num_splits=1, o_part=None, lse_part=None, o_lat=None, lse=None,
+                         stream=None):
+    """Latent attention over the FP8 cache (see mla.h); q_lat bf16 [B*q_len, n_h, 576]."""
+    torch = _torch()
+    _fp8_cache(kv_cache, kv_scale)
+    if q_lat.dtype != torch.bfloat16:
+        raise TypeError("q_lat must be bf16")
+    B = int(seq_lens.shape[0])
+    n_h = int(q_lat.shape[-2])
+    if q_lat.shape[-1] != ROW or q_lat.numel() != B * q_len * n_h * ROW:
+        raise ValueError("q_lat must hold [B, q_len, n_h, 576]")
+    rows = B * q_len * n_h
+    if int(num_splits) > 1:
+        if o_part is None or lse_part is None or o_part.numel() != rows * num_splits * D_C \
+                or lse_part.numel() != rows * num_splits:
+            raise ValueError("o_part / lse_part must hold [B, S, q_len, n_h, 512] / [B, S, q_len, n_h]")
+    elif o_lat is None or lse is None or o_lat.numel() != rows * D_C or lse.numel() != rows:
+        raise ValueError("o_lat / lse must hold [B, q_len, n_h, 512] / [B, q_len, n_h]")
+    f32 = torch.float32
+    st = load().mla_decode_paged_fp8(
+        _dev(q_lat, "q_lat"), _dev(kv_cache, "kv_cache"), _dev(kv_scale, "kv_scale"),
+        int(kv_cache.shape[0]), int(kv_cache.shape[1]),
+        _dev(block_table, "block_table", torch.int32), int(block_table.shape[1]),
+        _dev(seq_lens, "seq_lens", torch.int32), B, int(q_len), n_h, float(softmax_scale),
+        int(num_splits), _dev(o_part, "o_part", f32), _dev(lse_part, "lse_part", f32),
+        _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32), _stream(stream))
+    _check("mla_decode_paged_fp8", st)
+
+
+def mla_decode_paged_planned_fp8(q_lat, kv_cache, kv_scale, block_table, B, q_len, softmax_scale,
+                                 work, o_lat, lse, o_part=None, lse_part=None, stream=None):
+    """mla_decode_paged_planned over the FP8 cache (see mla.h)."""
+    torch = _torch()
+    _fp8_cache(kv_cache, kv_scale)
+    if q_lat.dtype != torch.bfloat16:
+        raise TypeError("q_lat must be bf16")
+    n_h = int(q_lat.shape[-2])
+    rows = int(B) * int(q_len)
+    if q_lat.shape[-1] != ROW or q_lat.numel() != rows * n_h * ROW:
+        raise ValueError("q_lat must hold [B, q_len, n_h, 576]")
+    if work.dim() != 2 or work.shape[1] != 4:
+        raise ValueError("work must be [n_work, 4]")
+    if o_lat.numel() != rows * n_h * D_C or lse.numel() != rows * n_h:
+        raise ValueError("o_lat / lse must hold [B, q_len, n_h, 512] / [B, q_len, n_h]")
+    if o_part is not None and (o_part.shape[-1] != D_C or o_part.numel() % (n_h * D_C) or
+                               lse_part is None or lse_part.numel() * D_C != o_part.numel()):
+        raise ValueError("o_part / lse_part must be [n_parts, n_h, 512] / [n_parts, n_h]")
+    n_parts = int(o_part.shape[0]) if o_part is not None else 0
+    f32 = torch.float32
+    st = load().mla_decode_paged_planned_fp8(
+        _dev(q_lat, "q_lat"), _dev(kv_cache, "kv_cache"), _dev(kv_scale, "kv_scale"),
+        int(kv_cache.shape[0]), int(kv_cache.shape[1]),
+        _dev(block_table, "block_table", torch.int32), int(block_table.shape[1]), int(B),
+        int(q_len), n_h, float(softmax_scale), _dev(work, "work", torch.int32),
+        int(work.shape[0]), _dev(o_part, "o_part", f32), _dev(lse_part, "lse_part", f32),
+        n_parts, _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32), _stream(stream))
+    _check("mla_decode_paged_planned_fp8", st)

@@ -125,6 +125,81 @@ int32_t mla_decode_paged(const void* q_lat, const void* kv_cache, int32_t num_bl
                                        (int)n_parts, (hipStream_t)stream));
 }
 
+int32_t mla_kv_append_fp8(void* kv_cache, float* kv_scale, int32_t dtype, int32_t num_blocks,
+                          int32_t block_size, const int32_t* block_table, int32_t num_seqs,
+                          int32_t max_blocks, const void* c_kv, const void* k_rope,
+                          const int32_t* seq_idx, const int32_t* pos, int32_t n, float rope_base,
+                          const double* rope_theta, void* stream) {
+  if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  mla::RopeFreq rf;
+  if (n < 0 || num_blocks < 1 || num_seqs < 1 || max_blocks < 1 || block_size != MLA_BLOCK ||
+      !mla::rope_freq(rope_base, rope_theta, rf))
+    return MLA_ERR_SHAPE;
+  if (n == 0) return MLA_OK;
+  if (!kv_cache || !kv_scale || !block_table || !c_kv || !k_rope || !seq_idx || !pos)
+    return MLA_ERR_NULL;
+  if (!aligned16(kv_cache) || !aligned16(kv_scale)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_kv_append_fp8(kv_cache, kv_scale, dtype, num_blocks, block_table,
+                                              num_seqs, max_blocks, c_kv, k_rope, seq_idx, pos,
+                                              n, rf, (hipStream_t)stream));
+}
+
+int32_t mla_decode_paged_fp8(const void* q_lat, const void* kv_cache, const float* kv_scale,
+                             int32_t num_blocks, int32_t block_size, const int32_t* block_table,
+                             int32_t max_blocks, const int32_t* seq_lens, int32_t B,
+                             int32_t q_len, int32_t n_h, float softmax_scale, int32_t num_splits,
+                             float* o_part, float* lse_part, float* o_lat, float* lse,
+                             void* stream) {
+  if (B < 0 || q_len < 1 || num_blocks < 1 || max_blocks < 1 || block_size != MLA_BLOCK ||
+      !decode_heads_ok(n_h) || num_splits < 1 || !(softmax_scale > 0.0f))
+    return MLA_ERR_SHAPE;
+  if ((int64_t)B * q_len * num_splits > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  if (B == 0) return MLA_OK;
+  if (!q_lat || !kv_cache || !kv_scale || !block_table || !seq_lens) return MLA_ERR_NULL;
+  float* o_out = o_lat;
+  float* l_out = lse;
+  if (num_splits > 1) {
+    if (!o_part || !lse_part) return MLA_ERR_NULL;
+    o_out = o_part;
+    l_out = lse_part;
+  } else if (!o_lat || !lse) {
+    return MLA_ERR_NULL;
+  }
+  if (!aligned16(q_lat) || !aligned16(kv_cache) || !aligned16(kv_scale) || !aligned16(o_out) ||
+      !aligned4(l_out))
+    return MLA_ERR_ALIGN;
+  const int64_t n_parts = num_splits > 1 ? (int64_t)B * q_len * num_splits : 0;
+  return hip_status(mla::launch_decode_fp8(q_lat, kv_cache, kv_scale, num_blocks, block_table,
+                                           max_blocks, seq_lens, B, q_len, n_h, softmax_scale,
+                                           num_splits, nullptr, 0, o_lat, lse, o_part, lse_part,
+                                           (int)n_parts, (hipStream_t)stream));
+}
+
+int32_t mla_decode_paged_planned_fp8(const void* q_lat, const void* kv_cache,
+                                     const float* kv_scale, int32_t num_blocks,
+                                     int32_t block_size, const int32_t* block_table,
+                                     int32_t max_blocks, int32_t B, int32_t q_len, int32_t n_h,
+                                     float softmax_scale, const int32_t* work, int32_t n_work,
+                                     float* o_part, float* lse_part, int32_t n_parts,
+                                     float* o_lat, float* lse, void* stream) {
+  if (B < 0 || q_len < 1 || num_blocks < 1 || max_blocks < 1 || block_size != MLA_BLOCK ||
+      !decode_heads_ok(n_h) || n_work < 0 || n_parts < 0 || !(softmax_scale > 0.0f))
+    return MLA_ERR_SHAPE;
+  if ((int64_t)B * q_len > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  if (n_work == 0 || B == 0) return MLA_OK;
+  if (!q_lat || !kv_cache || !kv_scale || !block_table || !work || !o_lat || !lse)
+    return MLA_ERR_NULL;
+  if (n_parts > 0 && (!o_part || !lse_part)) return MLA_ERR_NULL;
+  if (!aligned16(q_lat) || !aligned16(kv_cache) || !aligned16(kv_scale) || !aligned16(o_lat) ||
+      !aligned4(lse) || !aligned16(work) || (o_part && !aligned16(o_part)) ||
+      (lse_part && !aligned4(lse_part)))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_decode_fp8(q_lat, kv_cache, kv_scale, num_blocks, block_table,
+                                           max_blocks, nullptr, B, q_len, n_h, softmax_scale, 1,
+                                           work, n_work, o_lat, lse, o_part, lse_part, n_parts,
+                                           (hipStream_t)stream));
+}
+
 int32_t mla_plan_decode(const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t block_size,
                         int32_t n_h, int32_t num_slots, int32_t max_work, int32_t* work,
                         int32_t* n_work, int32_t* lists, int32_t* n_lists, int32_t* split,

@@ -30,6 +30,13 @@ hipError_t launch_kv_append(void* cache, int dtype, int num_blocks, const int* t
                             const int* seq_idx, const int* pos, int n, const RopeFreq& rf,
                             hipStream_t stream);
 
+// FP8 E4M3 cache: rows of 576 code bytes [num_blocks, 64, 576] and two
+// float32 scales per row (latent, RoPE) [num_blocks, 64, 2].
+hipError_t launch_kv_append_fp8(void* cache, float* kv_scale, int dtype, int num_blocks,
+                                const int* table, int num_seqs, int max_blocks, const void* c_kv,
+                                const void* k_rope, const int* seq_idx, const int* pos, int n,
+                                const RopeFreq& rf, hipStream_t stream);
+
 hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
                            const int* q_pos, int T, int n_h, int dtype, const RopeFreq& rf,
                            void* q_lat, hipStream_t stream);
@@ -52,6 +59,14 @@ hipError_t launch_decode_h64(const void* q_lat, const void* cache, int num_block
                              const int* table, int max_blocks, const int* seq_lens, int B,
                              int q_len, int n_h, float scale, int S, const int* work, int n_work,
                              const int* lists, int n_lists, float* o_lat, float* lse,
+                             float* o_part, float* lse_part, int n_parts, hipStream_t stream);
+
+// FP8 E4M3 cache with per-row scales (decode_fp8.hip); queries bf16; any
+// head count the bf16 kernels take; one item per workgroup.
+hipError_t launch_decode_fp8(const void* q_lat, const void* cache, const float* kv_scale,
+                             int num_blocks, const int* table, int max_blocks,
+                             const int* seq_lens, int B, int q_len, int n_h, float scale, int S,
+                             const int* work, int n_work, float* o_lat, float* lse,
                              float* o_part, float* lse_part, int n_parts, hipStream_t stream);
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int B, int S, int q_len,

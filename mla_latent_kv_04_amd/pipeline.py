@@ -34,6 +34,8 @@ class DeviceProblem:
     num_splits > 0: uniform split-KV with that many splits per row.
     num_splits == 0: a load-balanced schedule from mla_plan_decode (``work``,
     ``lists``, ``split``) sized for ``num_slots`` concurrent workgroups.
+    kv_scale is None for a bf16 / fp32 cache; for the FP8 cache kv_cache holds
+    uint8 E4M3 codes and kv_scale the two float32 scales of every row.
     """
     prob: Problem
     num_splits: int
@@ -60,6 +62,7 @@ class DeviceProblem:
     lists: Optional[object] = None
     split: Optional[object] = None
     n_parts: int = 0
+    kv_scale: Optional[object] = None
 
     @property
     def B(self):
@@ -93,17 +96,31 @@ def device_slots(device="cuda") -> int:
 
 
 def upload(prob: Problem, num_splits: Optional[int] = None, device="cuda",
-           poison: bool = True, num_slots: Optional[int] = None) -> DeviceProblem:
+           poison: bool = True, num_slots: Optional[int] = None,
+           cache: str = "native") -> DeviceProblem:
     """Copy a generated problem to the GPU and fill the cache with every row the
     step does not append itself (with the library's own append kernel).
 
-    num_splits None -> the workload's own; 0 -> a balanced work plan."""
+    num_splits None -> the workload's own; 0 -> a balanced work plan.
+    cache "native" keeps rows in the workload's dtype; "fp8" quantises them
+    (bf16 workloads only)."""
     torch = _torch()
     wl = prob.wl
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     S = wl.num_splits if num_splits is None else int(num_splits)
-    fill = float("nan") if poison else 0.0
-    kv_cache = torch.full((prob.num_blocks, BLOCK, ROW), fill, dtype=dt, device=device)
+    fp8 = cache == "fp8"
+    if fp8 and wl.dtype != "bf16":
+        raise ValueError("the FP8 cache takes bf16 queries")
+    if fp8:
+        # poison: 0xFF is the E4M3 NaN code
+        kv_cache = torch.full((prob.num_blocks, BLOCK, ROW), 0xFF if poison else 0,
+                              dtype=torch.uint8, device=device)
+        kv_scale = torch.full((prob.num_blocks, BLOCK, 2), float("nan") if poison else 1.0,
+                              dtype=torch.float32, device=device)
+    else:
+        fill = float("nan") if poison else 0.0
+        kv_cache = torch.full((prob.num_blocks, BLOCK, ROW), fill, dtype=dt, device=device)
+        kv_scale = None
     block_table = torch.from_numpy(prob.block_table).to(device)
     seq_lens = torch.from_numpy(prob.seq_lens).to(device)
 
@@ -117,17 +134,22 @@ def upload(prob: Problem, num_splits: Optional[int] = None, device="cuda",
     chunk = 1 << 18
     for lo in range(0, len(old), chunk):
         idx = old[lo:lo + chunk]
-        mla.mla_kv_append(kv_cache, block_table, _to_device(prob.c_kv[idx], dt, device),
-                          _to_device(prob.k_r[idx], dt, device),
-                          torch.from_numpy(seq_of_row[idx].astype(np.int32)).to(device),
-                          torch.from_numpy(pos_of_row[idx].astype(np.int32)).to(device),
-                          ROPE_BASE)
+        args = (block_table, _to_device(prob.c_kv[idx], dt, device),
+                _to_device(prob.k_r[idx], dt, device),
+                torch.from_numpy(seq_of_row[idx].astype(np.int32)).to(device),
+                torch.from_numpy(pos_of_row[idx].astype(np.int32)).to(device), ROPE_BASE)
+        if fp8:
+            mla.mla_kv_append_fp8(kv_cache, kv_scale, *args)
+        else:
+            mla.mla_kv_append(kv_cache, *args)
     new_idx = prob.key_offsets[step_seq] + step_pos
     T = prob.T
     work = lists = split = None
     n_parts = 0
     if S == 0:
-        slots = device_slots(device) if num_slots is None else int(num_slots)
+        # the FP8 kernel runs two workgroups per compute unit below 64 heads
+        per_cu = 2 if fp8 and wl.n_h < 64 else 1
+        slots = per_cu * device_slots(device) if num_slots is None else int(num_slots)
         w, ls, sp, n_parts = mla.mla_plan_decode(prob.seq_lens, wl.q_len, wl.n_h, slots)
         work = torch.from_numpy(w).to(device)
         lists = torch.from_numpy(ls).to(device)
@@ -151,17 +173,26 @@ def upload(prob: Problem, num_splits: Optional[int] = None, device="cuda",
         o_lat=torch.empty((T, wl.n_h, D_C), dtype=torch.float32, device=device),
         lse=torch.empty((T, wl.n_h), dtype=torch.float32, device=device),
         out=torch.empty((T, wl.n_h, D_H), dtype=torch.float32, device=device),
-        work=work, lists=lists, split=split, n_parts=n_parts,
+        work=work, lists=lists, split=split, n_parts=n_parts, kv_scale=kv_scale,
     )
     return dp
+
+
+def append(dp: DeviceProblem, stream=None):
+    """The step's new rows into the cache (quantised for the FP8 cache)."""
+    if dp.kv_scale is not None:
+        mla.mla_kv_append_fp8(dp.kv_cache, dp.kv_scale, dp.block_table, dp.new_c_kv, dp.new_k_r,
+                              dp.new_seq, dp.new_pos, ROPE_BASE, stream=stream)
+    else:
+        mla.mla_kv_append(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r, dp.new_seq,
+                          dp.new_pos, ROPE_BASE, stream=stream)
 
 
 def step(dp: DeviceProblem, stream=None):
     """One pass of the hot path: append -> absorb -> decode -> combine -> out-proj.
     Under a balanced plan the combine runs inside the out-projection's loads
     (dp.o_lat then holds only the rows the plan did not split)."""
-    mla.mla_kv_append(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r, dp.new_seq,
-                      dp.new_pos, ROPE_BASE, stream=stream)
+    append(dp, stream)
     mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE, stream=stream)
     if dp.num_splits == 0:
         _attend_planned(dp, stream)
@@ -190,6 +221,11 @@ def step_non_absorbed(dp: DeviceProblem, workspace, stream=None):
 
 
 def _attend_planned(dp: DeviceProblem, stream=None):
+    if dp.kv_scale is not None:
+        mla.mla_decode_paged_planned_fp8(dp.q_lat, dp.kv_cache, dp.kv_scale, dp.block_table, dp.B,
+                                         dp.q_len, softmax_scale(), dp.work, dp.o_lat, dp.lse,
+                                         o_part=dp.o_part, lse_part=dp.lse_part, stream=stream)
+        return
     mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
                                  softmax_scale(), dp.work, dp.o_lat, dp.lse,
                                  o_part=dp.o_part, lse_part=dp.lse_part, lists=dp.lists,
@@ -204,6 +240,13 @@ def decode(dp: DeviceProblem, stream=None):
         if dp.split.shape[0] > 0:
             mla.mla_combine_planned(dp.o_part, dp.lse_part, dp.split, dp.n_h, dp.o_lat, dp.lse,
                                     stream=stream)
+    elif dp.kv_scale is not None:
+        mla.mla_decode_paged_fp8(dp.q_lat, dp.kv_cache, dp.kv_scale, dp.block_table, dp.seq_lens,
+                                 dp.q_len, softmax_scale(), S, o_part=dp.o_part,
+                                 lse_part=dp.lse_part, o_lat=dp.o_lat, lse=dp.lse, stream=stream)
+        if S > 1:
+            mla.mla_splitkv_combine(dp.o_part, dp.lse_part, dp.B, S, dp.q_len, dp.n_h, dp.o_lat,
+                                    dp.lse, stream=stream)
     elif S > 1:
         mla.mla_decode_paged(dp.q_lat, dp.kv_cache, dp.block_table, dp.seq_lens, dp.q_len,
                              softmax_scale(), S, o_part=dp.o_part, lse_part=dp.lse_part,
