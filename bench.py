@@ -33,6 +33,7 @@ PRODUCER_EPS = 1e-6           # RMSNorm epsilon of the latent and query norms
 # sources of the attention kernels; the committed HBM-traffic record is only
 # used while these are unchanged
 DECODE_SOURCES = ["mla_latent_kv_04_amd/csrc/decode.hip", "mla_latent_kv_04_amd/csrc/decode_h64.hip",
+                  "mla_latent_kv_04_amd/csrc/decode_fp8.hip",
                   "mla_latent_kv_04_amd/csrc/mla_common.h", "mla_latent_kv_04_amd/csrc/mla_api.cpp"]
 
 
@@ -48,16 +49,18 @@ def source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_work(prob):
+def algorithmic_work(prob, fp8=False):
     """(bytes, flops) one attention-kernel launch must move / perform.
 
-    Bytes: every visible cached row once (576 elements), the latent queries
-    once, and the fp32 output (512 + 1 per row and head).  FLOPs: 2 * 576 for
-    the score plus 2 * 512 for the weighted sum, per (query row, head, key).
+    Bytes: every visible cached row once (576 elements; with the FP8 cache 576
+    code bytes and two float32 scales), the latent queries once, and the fp32
+    output (512 + 1 per row and head).  FLOPs: 2 * 576 for the score plus
+    2 * 512 for the weighted sum, per (query row, head, key).
     """
     import numpy as np
     wl = prob.wl
     esz = 2 if wl.dtype == "bf16" else 4
+    row_bytes = 576 + 8 if fp8 else 576 * esz
     keys_read = int(np.sum(prob.seq_lens.astype(np.int64)))          # each row read once
     pairs = 0
     for b in range(wl.B):
@@ -65,14 +68,15 @@ def algorithmic_work(prob):
         q = wl.q_len
         pairs += sum(max(0, L - (q - 1 - m)) for m in range(q))
     T = prob.T
-    by = keys_read * 576 * esz + T * wl.n_h * 576 * esz + T * wl.n_h * 513 * 4
+    by = keys_read * row_bytes + T * wl.n_h * 576 * esz + T * wl.n_h * 513 * 4
     fl = pairs * wl.n_h * (2 * 576 + 2 * 512)
     return by, fl
 
 
 def load_traffic(workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source (else None)."""
+    taken on the current kernel source (else None).  workload: the workload's
+    name, with "_fp8" for the FP8 cache."""
     path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -116,10 +120,12 @@ def producer_work(T, n_h, d_model, d_cq, esz):
     return kv_by, q_by, 2 * T * kv_w, 2 * T * q_w
 
 
-def cpu_baseline(prob, budget_s: float, hid=None):
+def cpu_baseline(prob, budget_s: float, hid=None, fp8=False):
     """Time the float64 oracle on whole sequences (all heads) until the budget
     is spent; returns tokens/s over the sample.  With hidden states, each
-    sequence's new row and queries come from the oracle's producers first."""
+    sequence's new row and queries come from the oracle's producers first.
+    With the FP8 cache, the oracle quantises the sequence's rows and attends
+    over their dequantised values (absorbed form)."""
     import numpy as np
     from oracle import mla_oracle as orc
     from mla_latent_kv_04_amd.workloads import ROPE_BASE, softmax_scale
@@ -153,9 +159,17 @@ def cpu_baseline(prob, budget_s: float, hid=None):
             else:
                 _, q_nope, q_rope = orc.q_produce(hid.h[sl], hid.w_dq, hid.q_gain, hid.w_uq,
                                                   hid.w_qr, wl.n_h, PRODUCER_EPS)
-        o, _, _ = orc.mla_attention_naive(c[:L], k[:L], q_nope, q_rope, prob.w_uk, prob.w_uv,
-                                          np.arange(L), prob.q_pos[sl], vis[:rows_per_call],
-                                          softmax_scale(), ROPE_BASE)
+        if fp8:
+            codes, sc = orc.kv_cache_rows_fp8(c[:L], k[:L], np.arange(L), ROPE_BASE)
+            rows = orc.dequantize_rows(codes, sc, 512)
+            q_lat = orc.absorb_query(q_nope, q_rope, prob.w_uk, prob.q_pos[sl], ROPE_BASE)
+            o_lat, _ = orc.latent_attention(q_lat, rows, vis[:rows_per_call], softmax_scale(),
+                                            512)
+            o = orc.out_projection(o_lat, prob.w_uv)
+        else:
+            o, _, _ = orc.mla_attention_naive(c[:L], k[:L], q_nope, q_rope, prob.w_uk,
+                                              prob.w_uv, np.arange(L), prob.q_pos[sl],
+                                              vis[:rows_per_call], softmax_scale(), ROPE_BASE)
         if hid is not None and hid.w_o is not None:
             orc.o_projection(o, hid.w_o)                  # eq. 8, as the step ends
         done_rows += rows_per_call
@@ -165,7 +179,9 @@ def cpu_baseline(prob, budget_s: float, hid=None):
             break
     dt = time.perf_counter() - t0
     sample = (f"{done_seqs} of {wl.B} sequences, {done_rows} query rows x {wl.n_h} heads, "
-              f"{keys} cached keys; non-absorbed float64 NumPy oracle")
+              f"{keys} cached keys; "
+              + ("float64 NumPy oracle: quantise, dequantise, absorbed attention" if fp8 else
+                 "non-absorbed float64 NumPy oracle"))
     return {"value": done_rows / dt, "unit": "tokens/s", "cores": cores,
             "blas_threads": threads, "kind": "oracle", "sample": sample,
             "seconds": round(dt, 2)}
@@ -205,6 +221,15 @@ def main():
     ap.add_argument("--from-hidden", action="store_true",
                     help="start the step from hidden states: the cache-row and query producers "
                          "(V2 or V2-Lite widths) replace the append and the given queries")
+    ap.add_argument("--cache", choices=("native", "fp8"), default="native",
+                    help="latent cache format: the workload's dtype, or FP8 E4M3 codes with two "
+                         "float32 scales per row (bf16 absorbed decode workloads)")
+    ap.add_argument("--launch", choices=("replay", "eager", "graph"), default="replay",
+                    help="replay: the step's library calls are marshalled once and re-issued "
+                         "each step without the Python wrappers' checks; eager: through the "
+                         "wrappers every step; graph: the timed steps replay a HIP graph of "
+                         "one step and the attention kernel is timed over replays of a graph "
+                         "of that kernel alone")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run one plain device-to-device copy of this many bytes (a "
                          "known-size reference for hardware byte counters)")
@@ -228,6 +253,11 @@ def main():
     if non_absorbed and (wl.q_len == 1 or wl.dtype != "bf16"):
         print("--attention non-absorbed is for bf16 chunked prefill workloads", file=sys.stderr)
         sys.exit(2)
+    fp8 = args.cache == "fp8"
+    if fp8 and (wl.dtype != "bf16" or non_absorbed or args.from_hidden):
+        print("--cache fp8 is for bf16 workloads in the absorbed form, from latent rows",
+              file=sys.stderr)
+        sys.exit(2)
     # V2 (128 heads): hidden 5120, queries through c^Q (1536); V2-Lite (16
     # heads): hidden 2048, queries straight from h
     d_model, d_cq = (D_MODEL_V2, D_CQ_V2) if wl.n_h == 128 else (D_MODEL_LITE, None)
@@ -235,7 +265,7 @@ def main():
     log(f"[bench] generating {wl.name} (splits={splits})")
     prob = make_problem(wl)
     torch.cuda.set_device(0)
-    dp = pipeline.upload(prob, num_splits=splits)
+    dp = pipeline.upload(prob, num_splits=splits, cache=args.cache)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     scale = softmax_scale()
@@ -265,15 +295,12 @@ def main():
                               dp.new_pos, ROPE_BASE)
             if ev is not None:
                 ev[0].record(stream)
-            mla.mla_prefill_mha(dp.q_nope, dp.q_rope, dp.q_pos, dp.w_uk, dp.w_uv, dp.kv_cache,
-                                dp.block_table, prob.seq_lens, dp.q_len, scale, ROPE_BASE,
-                                dp.out, dp.lse, pf_ws)
+            attend()
             if ev is not None:
                 ev[1].record(stream)
             return
         if hw is None:
-            mla.mla_kv_append(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r, dp.new_seq,
-                              dp.new_pos, ROPE_BASE)
+            pipeline.append(dp)
         else:
             if ev is not None:
                 ev[2].record(stream)
@@ -292,16 +319,7 @@ def main():
         mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE)
         if ev is not None:
             ev[0].record(stream)
-        if splits == 0:
-            mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
-                                         scale, dp.work, dp.o_lat, dp.lse, o_part=dp.o_part,
-                                         lse_part=dp.lse_part, lists=dp.lists)
-        elif splits > 1:
-            mla.mla_decode_paged(dp.q_lat, dp.kv_cache, dp.block_table, dp.seq_lens, dp.q_len,
-                                 scale, splits, o_part=dp.o_part, lse_part=dp.lse_part)
-        else:
-            mla.mla_decode_paged(dp.q_lat, dp.kv_cache, dp.block_table, dp.seq_lens, dp.q_len,
-                                 scale, 1, o_lat=dp.o_lat, lse=dp.lse)
+        attend()
         if ev is not None:
             ev[1].record(stream)
         if splits == 0:
@@ -320,6 +338,31 @@ def main():
                                     dp.o_lat, dp.lse)
         mla.mla_out_proj(dp.o_lat, dp.w_uv, dp.out)
 
+    def attend():
+        """The attention kernel of the step (the dominant kernel)."""
+        if non_absorbed:
+            mla.mla_prefill_mha(dp.q_nope, dp.q_rope, dp.q_pos, dp.w_uk, dp.w_uv, dp.kv_cache,
+                                dp.block_table, prob.seq_lens, dp.q_len, scale, ROPE_BASE,
+                                dp.out, dp.lse, pf_ws)
+        elif fp8 and splits == 0:
+            mla.mla_decode_paged_planned_fp8(dp.q_lat, dp.kv_cache, dp.kv_scale, dp.block_table,
+                                             dp.B, dp.q_len, scale, dp.work, dp.o_lat, dp.lse,
+                                             o_part=dp.o_part, lse_part=dp.lse_part)
+        elif fp8:
+            mla.mla_decode_paged_fp8(dp.q_lat, dp.kv_cache, dp.kv_scale, dp.block_table,
+                                     dp.seq_lens, dp.q_len, scale, splits, o_part=dp.o_part,
+                                     lse_part=dp.lse_part, o_lat=dp.o_lat, lse=dp.lse)
+        elif splits == 0:
+            mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
+                                         scale, dp.work, dp.o_lat, dp.lse, o_part=dp.o_part,
+                                         lse_part=dp.lse_part, lists=dp.lists)
+        elif splits > 1:
+            mla.mla_decode_paged(dp.q_lat, dp.kv_cache, dp.block_table, dp.seq_lens, dp.q_len,
+                                 scale, splits, o_part=dp.o_part, lse_part=dp.lse_part)
+        else:
+            mla.mla_decode_paged(dp.q_lat, dp.kv_cache, dp.block_table, dp.seq_lens, dp.q_len,
+                                 scale, 1, o_lat=dp.o_lat, lse=dp.lse)
+
     if args.copy_bytes > 0:
         n = args.copy_bytes // 4
         src = torch.arange(n, dtype=torch.int32, device="cuda")
@@ -329,6 +372,38 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] reference copy of {4 * n} bytes done")
         del src, dst
+
+    if args.launch != "eager":
+        # Checked once through the wrappers, then recorded: the timed loop
+        # re-issues the marshalled calls, so that the CPU stays ahead of the
+        # GPU (the wrappers' per-call checks cost more than a small step's
+        # kernels and would leave the GPU idle between them, inside the
+        # events that time the attention kernel).
+        one_step()
+        torch.cuda.synchronize()
+
+        class _Mark:
+            def __init__(self, rec, k):
+                self.rec, self.k = rec, k
+
+            def record(self, _stream):
+                self.rec.calls.append(("__event__", self.k))
+
+        with mla.recording() as rec:
+            one_step(tuple(_Mark(rec, k) for k in range(7)))
+        step_calls = rec.calls
+        lib = mla.load()
+        checked_step = one_step
+
+        def one_step(ev=None):
+            for name, a in step_calls:
+                if name == "__event__":
+                    if ev is not None:
+                        ev[a].record(stream)
+                    continue
+                st = getattr(lib, name)(*a)
+                if st != 0:
+                    raise mla.MLAError(name, st, mla.status_string(st))
 
     log(f"[bench] warmup {args.warmup}")
     tw = time.perf_counter()
@@ -357,10 +432,43 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     dec_times = [e[0].elapsed_time(e[1]) for e in events]
+    timing = {"launch": args.launch, "warmup_steps": args.warmup, "settle_steps": settle}
+    if args.launch == "graph":
+        # Eager launches from Python cost tens of microseconds each, more than a
+        # small step's kernels: the GPU then idles between them.  A graph of one
+        # step is replayed instead (one launch per step); the attention kernel is
+        # timed over back-to-back replays of a graph holding it alone.
+        timing["unreplayed_step_ms"] = round(ms_per_step, 5)
+        timing["attention_in_step_us"] = spread(dec_times)
+        g_step, g_att = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            checked_step()
+        with torch.cuda.graph(g_att):
+            attend()
+        for _ in range(20):
+            g_step.replay()
+            g_att.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step_ev[i][0].record(stream)
+            g_step.replay()
+            step_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / args.steps
+        att_ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
+                  for _ in range(args.steps)]
+        for i in range(args.steps):
+            att_ev[i][0].record(stream)
+            g_att.replay()
+            att_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        dec_times = [e[0].elapsed_time(e[1]) for e in att_ev]
+        del g_step, g_att
     dec_ms = float(np.mean(dec_times))
-    timing = {"attention_us": spread(dec_times),
-              "step_us": spread([e[0].elapsed_time(e[1]) for e in step_ev]),
-              "warmup_steps": args.warmup, "settle_steps": settle}
+    timing["attention_us"] = spread(dec_times)
+    timing["step_us"] = spread([e[0].elapsed_time(e[1]) for e in step_ev])
     if args.cold_steps > 0:
         # each step after a 1 GiB write: the cache rows, queries and weights
         # come from HBM, not from the L2 / last-level cache
@@ -376,14 +484,14 @@ def main():
     tokens = prob.T
     value = tokens / (ms_per_step * 1e-3)
 
-    by, fl = algorithmic_work(prob)
+    by, fl = algorithmic_work(prob, fp8)
     if non_absorbed:
         fl = non_absorbed_flops(prob)
     compute_bound = wl.q_len > 1
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     gbs = by / (dec_ms * 1e-3) / 1e9
     tflops = fl / (dec_ms * 1e-3) / 1e12
-    traffic = load_traffic(wl.name)
+    traffic = load_traffic(wl.name + ("_fp8" if fp8 else ""))
     if compute_bound:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak,
                 "unit": "TFLOP/s", "frac": round(tflops / mfma_peak, 4), "traffic": traffic}
@@ -422,7 +530,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_seconds} s)")
-        cpu = cpu_baseline(prob, args.cpu_seconds, hid)
+        cpu = cpu_baseline(prob, args.cpu_seconds, hid, fp8)
 
     cfg = {"workload": wl.name, "B": wl.B, "n_h": wl.n_h, "q_len": wl.q_len,
            "context": (f"U[{wl.ctx[0]},{wl.ctx[1]}]" if isinstance(wl.ctx, tuple) else wl.ctx),
@@ -431,6 +539,7 @@ def main():
            "work_items": (int(dp.work.shape[0]) if splits == 0 else dp.B * dp.q_len * splits),
            "d_c": 512, "d_R": 64, "d_h": 128,
            "attention_form": args.attention,
+           "kv_cache": ("fp8 e4m3 codes + 2 fp32 scales per row" if fp8 else wl.dtype),
            "step_input": ("hidden states (cache-row and query producers in the step; the "
                           "step ends with eq. 8's W^O when the plan is balanced)"
                           if hw is not None else "new latent rows and per-head queries")}

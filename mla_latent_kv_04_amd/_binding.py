@@ -46,9 +46,61 @@ def lib_path() -> str:
     return LIB
 
 
+class _Recorder:
+    """Stands in for the library while calls are recorded: every entry point
+    call is kept as (name, arguments) and reports success."""
+
+    def __init__(self, lib):
+        self.lib = lib
+        self.calls = []
+
+    def __getattr__(self, name):
+        fn = getattr(self.lib, name)
+        if not name.startswith("mla_") or fn.restype is not _I or name == "mla_abi_version":
+            return fn
+
+        def record(*args):
+            self.calls.append((name, args))
+            return MLA_OK
+        return record
+
+
+_recorder: Optional[_Recorder] = None
+
+
+class recording:
+    """Context manager: the entry-point wrappers called inside it check and
+    marshal their arguments as usual but enqueue nothing; ``calls`` then holds
+    the marshalled calls, which ``replay`` issues again with no Python-side
+    checks (for launch loops where the wrappers' overhead would leave the GPU
+    idle).  The tensors and the stream the calls name must stay alive and
+    unchanged in shape."""
+
+    def __enter__(self):
+        global _recorder
+        _recorder = _Recorder(load())
+        return _recorder
+
+    def __exit__(self, *exc):
+        global _recorder
+        _recorder = None
+        return False
+
+
+def replay(calls):
+    """Issue recorded calls in order; raises MLAError on a non-OK status."""
+    lib = load()
+    for name, args in calls:
+        st = getattr(lib, name)(*args)
+        if st != MLA_OK:
+            raise MLAError(name, st, lib.mla_status_string(st).decode())
+
+
 def load() -> ctypes.CDLL:
     """Load the built library (raises if it was not built)."""
     global _lib
+    if _recorder is not None:
+        return _recorder
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB):
