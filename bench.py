@@ -211,6 +211,9 @@ def main():
                     help="extra steps, each after a 1 GiB write that evicts the caches, "
                          "timed separately (reported as cold; 0 = skip)")
     ap.add_argument("--workload", default="v2_bf16_B128_L1k-8k")
+    ap.add_argument("--q-len", type=int, default=None,
+                    help="query rows per sequence instead of the workload's (the rows are the "
+                         "last ones of each sequence; for the absorbed / non-absorbed crossover)")
     ap.add_argument("--splits", type=int, default=None,
                     help="split-KV partitions per row; 0 = balanced work plan (default: workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -249,9 +252,12 @@ def main():
                                                 softmax_scale)
 
     wl = WORKLOADS[args.workload]
+    if args.q_len is not None:
+        import dataclasses
+        wl = dataclasses.replace(wl, q_len=int(args.q_len))
     non_absorbed = args.attention == "non-absorbed"
-    if non_absorbed and (wl.q_len == 1 or wl.dtype != "bf16"):
-        print("--attention non-absorbed is for bf16 chunked prefill workloads", file=sys.stderr)
+    if non_absorbed and wl.dtype != "bf16":
+        print("--attention non-absorbed is for bf16 workloads", file=sys.stderr)
         sys.exit(2)
     fp8 = args.cache == "fp8"
     if fp8 and (wl.dtype != "bf16" or non_absorbed or args.from_hidden):

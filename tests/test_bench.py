@@ -25,9 +25,13 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
-def test_non_absorbed_attention_is_for_prefill_only():
-    r = _run("--attention", "non-absorbed", "--workload", "v2_bf16_B128_L1k-8k")
-    assert r.returncode == 2 and "prefill" in r.stderr
+def test_refused_combinations_exit_before_touching_the_gpu():
+    # the non-absorbed kernel is bf16 only; the FP8 cache serves the absorbed form
+    r = _run("--attention", "non-absorbed", "--workload", "v2lite_f32_L256")
+    assert r.returncode == 2 and "bf16" in r.stderr
+    r = _run("--cache", "fp8", "--attention", "non-absorbed", "--workload",
+             "v2_bf16_prefill_6144+2048")
+    assert r.returncode == 2 and "absorbed" in r.stderr
 
 
 def test_decode_work_counts_every_key_once():
