@@ -6,13 +6,47 @@
 // §2.1.1).  Splits that saw no key carry lse = -inf and weight 0.
 //
 // One workgroup per (row, pair of heads); a thread owns 4 of the 512 dims.
-// This pass is bandwidth bound: it reads S x 2 KB per head once.
+// This pass is bandwidth bound: it reads S x 2 KB per head once.  The parts
+// are read MERGE_BATCH at a time, all loads of a batch in flight together,
+// and summed in part order.
 #include "mla_common.h"
 #include "mla_internal.h"
 
 namespace mla {
 
 namespace {
+
+constexpr int MERGE_BATCH = 8;
+
+// sum_k w_k x_k and sum_k w_k over parts k = 0..count-1 at p(k) (element
+// offsets of the lse entries; the output row is D_C floats per lse entry),
+// w_k = exp(lse_k - mx), a part with lse -inf weighing nothing.
+template <class PartAt>
+__device__ __forceinline__ void merge_parts(const float* __restrict__ o_part,
+                                            const float* __restrict__ lse_part, int count,
+                                            PartAt part_at, float mx, int d4, float4& o, float& z) {
+  for (int k0 = 0; k0 < count; k0 += MERGE_BATCH) {
+    float w[MERGE_BATCH];
+    float4 x[MERGE_BATCH];
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u) {
+      w[u] = 0.0f;
+      x[u] = float4{0, 0, 0, 0};
+      if (k0 + u < count) {
+        const long pr = part_at(k0 + u);
+        const float l = lse_part[pr];
+        w[u] = l == -INFINITY ? 0.0f : __expf(l - mx);
+        x[u] = reinterpret_cast<const float4*>(o_part + pr * D_C)[d4];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u) {
+      if (w[u] == 0.0f) continue;
+      z += w[u];
+      o.x += w[u] * x[u].x; o.y += w[u] * x[u].y; o.z += w[u] * x[u].z; o.w += w[u] * x[u].w;
+    }
+  }
+}
 
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o_part,
                                                       const float* __restrict__ lse_part, int S,
@@ -27,19 +61,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   const long step = (long)q_len * n_h;    // distance between consecutive splits
   const long p0 = ((long)b * S * q_len + m) * n_h + head;
   float mx = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) mx = fmaxf(mx, lse_part[p0 + s * step]);
   float4 o = {0, 0, 0, 0};
   float z = 0.0f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float l = lse_part[p0 + s * step];
-      if (l == -INFINITY) continue;
-      const float w = __expf(l - mx);
-      z += w;
-      const float4 x = reinterpret_cast<const float4*>(o_part + (p0 + s * step) * D_C)[d4];
-      o.x += w * x.x; o.y += w * x.y; o.z += w * x.z; o.w += w * x.w;
-    }
-  }
+  if (mx != -INFINITY)
+    merge_parts(o_part, lse_part, S, [&](int s) { return p0 + s * step; }, mx, d4, o, z);
   const float inv = z > 0.0f ? 1.0f / z : 0.0f;
   reinterpret_cast<float4*>(o_lat + ((long)row * n_h + head) * D_C)[d4] =
       float4{o.x * inv, o.y * inv, o.z * inv, o.w * inv};
@@ -57,20 +84,13 @@ __global__ void __launch_bounds__(256) combine_planned_kernel(
   const int row = split[blockIdx.x * 3], first = split[blockIdx.x * 3 + 1];
   const int count = split[blockIdx.x * 3 + 2];
   float mx = -INFINITY;
+#pragma unroll 8
   for (int k = 0; k < count; ++k) mx = fmaxf(mx, lse_part[(long)(first + k) * n_h + head]);
   float4 o = {0, 0, 0, 0};
   float z = 0.0f;
-  if (mx != -INFINITY) {
-    for (int k = 0; k < count; ++k) {
-      const long pr = (long)(first + k) * n_h + head;
-      const float l = lse_part[pr];
-      if (l == -INFINITY) continue;
-      const float w = __expf(l - mx);
-      z += w;
-      const float4 x = reinterpret_cast<const float4*>(o_part + pr * D_C)[d4];
-      o.x += w * x.x; o.y += w * x.y; o.z += w * x.z; o.w += w * x.w;
-    }
-  }
+  if (mx != -INFINITY)
+    merge_parts(o_part, lse_part, count,
+                [&](int k) { return (long)(first + k) * n_h + head; }, mx, d4, o, z);
   const float inv = z > 0.0f ? 1.0f / z : 0.0f;
   reinterpret_cast<float4*>(o_lat + ((long)row * n_h + head) * D_C)[d4] =
       float4{o.x * inv, o.y * inv, o.z * inv, o.w * inv};

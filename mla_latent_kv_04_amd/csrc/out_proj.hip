@@ -306,6 +306,44 @@ __global__ void __launch_bounds__(256) out_proj_bf16_kernel(const float* __restr
   }
 }
 
+// Few query rows (T <= SMALL_T, bf16 weights): one wave per (head h, 16
+// outputs d0 .. d0 + 15, 16 rows t0 .. t0 + 15), so that the grid still
+// spreads over the chip.  The wave's 16 rows of W^UV_h and its 16 o_lat rows
+// (as bf16 hi + lo) are all loaded at once, straight from memory, then 32
+// MFMAs; each W^UV row is read by T / 16 waves, each o_lat row by 8.
+constexpr int SMALL_T = 64;
+
+__global__ void __launch_bounds__(64) out_proj_small_kernel(const float* __restrict__ o_lat,
+                                                            const uint16_t* __restrict__ w_uv,
+                                                            int T, int n_h,
+                                                            float* __restrict__ out) {
+  const int h = blockIdx.x, d0 = blockIdx.y * 16, t0 = blockIdx.z * 16;
+  const int lane = lane_id(), g = lane >> 4, r16 = lane & 15;
+  const int t = t0 + r16;
+  const uint16_t* wrow = w_uv + ((long)h * D_H + d0 + r16) * D_C + 8 * g;
+  const float* lrow = o_lat + ((long)t * n_h + h) * D_C + 8 * g;
+  BF16::frag wf[D_C / 32];
+  float4 lat[D_C / 32][2];
+#pragma unroll
+  for (int ks = 0; ks < D_C / 32; ++ks) {
+    wf[ks] = BF16::load8(wrow + ks * 32);
+    lat[ks][0] = t < T ? reinterpret_cast<const float4*>(lrow + ks * 32)[0] : float4{0, 0, 0, 0};
+    lat[ks][1] = t < T ? reinterpret_cast<const float4*>(lrow + ks * 32)[1] : float4{0, 0, 0, 0};
+  }
+  f32x4_t acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < D_C / 32; ++ks) {
+    BF16::frag lf[2];
+    LatFrag<BF16>::split(lat[ks][0], lat[ks][1], lf);
+    BF16::mma(acc, wf[ks], lf[0]);
+    BF16::mma(acc, wf[ks], lf[1]);
+  }
+  // lane holds row t and outputs d0 + 4g .. d0 + 4g + 3
+  if (t < T)
+    *reinterpret_cast<float4*>(out + ((long)t * n_h + h) * D_H + d0 + 4 * g) =
+        float4{acc[0], acc[1], acc[2], acc[3]};
+}
+
 template <class E>
 __global__ void __launch_bounds__(256) out_proj_kernel(const float* __restrict__ o_lat,
                                                        const typename E::storage* __restrict__ w_uv,
@@ -352,6 +390,11 @@ __global__ void __launch_bounds__(256) out_proj_kernel(const float* __restrict__
 hipError_t launch_out_proj(const float* o_lat, const void* w_uv, int T, int n_h, int dtype,
                            float* out, hipStream_t stream) {
   dim3 grid(n_h, (T + TCH - 1) / TCH), block(256);
+  if (dtype == 1 && T <= SMALL_T) {
+    hipLaunchKernelGGL(out_proj_small_kernel, dim3(n_h, D_H / 16, (T + 15) / 16), dim3(64), 0,
+                       stream, o_lat, (const uint16_t*)w_uv, T, n_h, out);
+    return hipGetLastError();
+  }
   if (dtype == 1) {
     // about two workgroups per CU of (head, chunk) pairs; each stages W^UV_h
     // once for all of its chunks
@@ -368,8 +411,9 @@ hipError_t launch_out_proj(const float* o_lat, const void* w_uv, int T, int n_h,
 hipError_t launch_out_proj_planned(float* o_lat, const float* o_part, const float* lse_part,
                                    const int* split, int n_split, const void* w_uv, int T, int n_h,
                                    int dtype, float* out, float* lse, hipStream_t stream) {
-  if (dtype != 1 || n_split == 0) {
-    // fp32 weights: merge into o_lat, then the plain projection
+  if (dtype != 1 || n_split == 0 || T <= SMALL_T) {
+    // fp32 weights, or few rows: merge into o_lat (a pass over all split rows
+    // at once), then the plain projection
     if (n_split > 0) {
       const hipError_t st =
           launch_combine_planned(o_part, lse_part, split, n_split, n_h, o_lat, lse, stream);

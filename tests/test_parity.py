@@ -222,11 +222,12 @@ def test_combine_matches_oracle():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_out_proj_matches_oracle(dtype):
+@pytest.mark.parametrize("T", [37, 130])
+def test_out_proj_matches_oracle(dtype, T):
     import torch
     from mla_latent_kv_04_amd import _binding as mla
     rng = np.random.default_rng(4)
-    T, n_h = 37, 32
+    n_h = 32
     o_lat = rng.standard_normal((T, n_h, D_C)).astype(np.float32)
     w = (rng.standard_normal((n_h, 128, D_C)) / math.sqrt(D_C)).astype(np.float32)
     if dtype == "bf16":
@@ -244,7 +245,9 @@ def test_out_proj_matches_oracle(dtype):
 # waves, a wave with split and unsplit rows, more split rows than one 64-way
 # search round covers, every row split, and no split row.
 PLANNED_PROJ = [(300, 16, "bf16", 0.6), (2560, 16, "bf16", 0.6), (130, 32, "bf16", 1.0),
-                (300, 16, "f32", 0.6), (70, 16, "bf16", 0.0)]
+                (300, 16, "f32", 0.6), (70, 16, "bf16", 0.0),
+                # few rows: merge pass, then one wave per (head, 16 outputs, 16 rows)
+                (4, 128, "bf16", 1.0), (64, 16, "bf16", 0.6), (17, 32, "bf16", 0.5)]
 
 
 @pytest.mark.parametrize("T,n_h,dtype,frac", PLANNED_PROJ,
