@@ -24,24 +24,27 @@
 //     uses exactly the P of the numerator.  These waves also issue the
 //     direct-to-LDS loads of the tiles.
 //
-// Each SIMD holds one wave of each role, and each iteration a of the tile
-// loop has two phases, so that one role's VALU and LDS work overlaps the
-// other's MFMAs (the hardware interleaves the two waves):
+// Each SIMD holds one wave of each role; the hardware interleaves the two, so
+// that one role's VALU and LDS work overlaps the other's MFMAs.  Iteration a
+// of the tile loop has one workgroup barrier:
 //
 //   barrier A(a): tile a+1 has landed; P(a), its maxima and flags are in LDS;
 //                 tile a-1 is no longer read by anyone
-//   phase A  score: QK^T of tile a+1 (36 MFMAs per wave)
-//            value: P(a) and V(a) into registers, PV of the first half of
-//                   the dims (16 MFMAs), loads of tile a+3 into the stage of
-//                   tile a-1
-//   barrier B(a)
-//   phase B  score: softmax of tile a+1 (scale, mask, tile maxima, P(a+1)
-//                   against the running max, into the other P buffer)
-//            value: PV of the second half of the dims, and the P row sums
+//   score waves: QK^T of tile a+1 (36 MFMAs per wave), then its softmax step
+//                (scale, mask, tile maxima, P(a+1) against the running max,
+//                into the other P buffer, and the flags)
+//   value waves: P(a) and V(a) into registers, PV of the first dims, loads of
+//                tile a+3 into the stage of tile a-1, the rest of PV, and the
+//                P row sums
 //   [redo a] only if a score wave saw a score of tile a beat the running max
-//            by more than 2^8 (log2 domain): in phase A the score waves agree
-//            on the new max and rewrite P(a), then (one more barrier) the
-//            value waves rescale their accumulators before reading P(a).
+//            by more than 2^8 (log2 domain): the score waves agree on the new
+//            max and rewrite P(a), then (one more barrier) the value waves
+//            rescale their accumulators before reading P(a).
+//
+// P, the tile maxima and the flags alternate between two buffers by tile
+// parity, so the softmax of tile a+1 never touches what the value waves read
+// for tile a; a second barrier per tile between the two halves of each role's
+// work (an earlier form) bought nothing and cost 1.5%.
 //
 // Tiles are 32 tokens (half a paged block) in four LDS stages, loaded three
 // tiles ahead.
@@ -81,7 +84,8 @@ constexpr int IDCAP = 512;                   // block ids staged per chunk of an
 #ifndef QK_REDO_STEP
 #define QK_REDO_STEP 6
 #endif
-constexpr int PV_A = PV_PHASE_A;             // PV dim blocks (of 8) run in phase A
+
+constexpr int PV_A = PV_PHASE_A;             // PV dim blocks (of 8) run before the loads of tile a+3
 constexpr int QK_MID = QK_REDO_STEP;         // QK k-steps issued before the redo check
 
 // LDS map (bytes)
@@ -465,7 +469,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
           // tile a+1 (past the chunk: fully masked; written but never read)
           f32x4_t sc[2];
           qk(a + 1, hi_n, kbuf, sc, redo);
-          lds_sync();  // barrier B(a)
           softmax(a + 1, sc);
         }
         c0 = c1;
@@ -562,11 +565,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
           vm_wait<NDMA>();
           lds_sync();  // barrier A(a)
           const int par = ch.par(a);
-          // Every LDS read of phase A is issued at once: the flags, the block
-          // ids of tiles a+1 and a+3, P(a) and V(a).  P(a) changes only in a
-          // redo, which reads it again.  Then PV of dims 16db.. for db < PV_A,
-          // then the loads of tile a+3 (LDS reads this wave issues after a
-          // direct-to-LDS load queue behind it).  Phase B: the rest of PV.
+          // Every LDS read of the iteration is issued at once: the flags, the
+          // block ids of tiles a+1 and a+3, P(a) and V(a).  P(a) changes only
+          // in a redo, which reads it again.  Then PV of dims 16db.. for
+          // db < PV_A, then the loads of tile a+3 (LDS reads this wave issues
+          // after a direct-to-LDS load queue behind it), then the rest of PV.
           const int4 fl = *reinterpret_cast<const int4*>(flags + par * 4);
           const int src = a + 3 < c1 ? a + 3 : a;
           const int id_src = ch.id(src);
@@ -611,7 +614,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) decode_h64_kernel(
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb) mma_pv(acc[hb][db], vf[db], pf[hb]);
           issue(a + 3, src, nid);
-          lds_sync();  // barrier B(a): the score waves turn to their softmax
 #pragma unroll
           for (int db = PV_A; db < 8; ++db)
 #pragma unroll
