@@ -353,7 +353,8 @@ def main():
         elif fp8 and splits == 0:
             mla.mla_decode_paged_planned_fp8(dp.q_lat, dp.kv_cache, dp.kv_scale, dp.block_table,
                                              dp.B, dp.q_len, scale, dp.work, dp.o_lat, dp.lse,
-                                             o_part=dp.o_part, lse_part=dp.lse_part)
+                                             o_part=dp.o_part, lse_part=dp.lse_part,
+                                             lists=dp.lists)
         elif fp8:
             mla.mla_decode_paged_fp8(dp.q_lat, dp.kv_cache, dp.kv_scale, dp.block_table,
                                      dp.seq_lens, dp.q_len, scale, splits, o_part=dp.o_part,

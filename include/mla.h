@@ -472,7 +472,8 @@ int32_t mla_kv_append_fp8(void* kv_cache, float* kv_scale, int32_t dtype, int32_
  * multiplication by its s_latent (an MFMA operand), and the normaliser sums
  * those same weights divided by s_latent, so the output is an exact
  * weighted mean of the dequantised latents.  Head counts as in
- * mla_decode_paged; one workgroup per work item (no lists).
+ * mla_decode_paged; lists as in mla_decode_paged_planned (used with 64 heads
+ * or more).
  */
 int32_t mla_decode_paged_fp8(const void* q_lat, const void* kv_cache, const float* kv_scale,
                              int32_t num_blocks, int32_t block_size, const int32_t* block_table,
@@ -485,8 +486,9 @@ int32_t mla_decode_paged_planned_fp8(const void* q_lat, const void* kv_cache,
                                      int32_t block_size, const int32_t* block_table,
                                      int32_t max_blocks, int32_t B, int32_t q_len, int32_t n_h,
                                      float softmax_scale, const int32_t* work, int32_t n_work,
-                                     float* o_part, float* lse_part, int32_t n_parts,
-                                     float* o_lat, float* lse, void* stream);
+                                     const int32_t* lists, int32_t n_lists, float* o_part,
+                                     float* lse_part, int32_t n_parts, float* o_lat, float* lse,
+                                     void* stream);
 
 /*
  * mla_decode_paged_noalloc - for callers that cannot allocate device memory

@@ -138,7 +138,7 @@ def load() -> ctypes.CDLL:
         "mla_decode_paged_fp8": (_I, [_P, _P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _F, _I, _P, _P,
                                       _P, _P, _P]),
         "mla_decode_paged_planned_fp8": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _F, _P, _I,
-                                              _P, _P, _I, _P, _P, _P]),
+                                              _P, _I, _P, _P, _I, _P, _P, _P]),
         "mla_decode_paged_noalloc": (_I, [_P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F, _I,
                                           _P, _P, _P]),
         "mla_prefill_mha": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _I, _P, _I, _I, _I, _I, _F,
@@ -704,7 +704,8 @@ def mla_decode_paged_fp8(q_lat, kv_cache, kv_scale, block_table, seq_lens, q_len
 
 
 def mla_decode_paged_planned_fp8(q_lat, kv_cache, kv_scale, block_table, B, q_len, softmax_scale,
-                                 work, o_lat, lse, o_part=None, lse_part=None, stream=None):
+                                 work, o_lat, lse, o_part=None, lse_part=None, lists=None,
+                                 stream=None):
     """mla_decode_paged_planned over the FP8 cache (see mla.h)."""
     torch = _torch()
     _fp8_cache(kv_cache, kv_scale)
@@ -716,6 +717,8 @@ def mla_decode_paged_planned_fp8(q_lat, kv_cache, kv_scale, block_table, B, q_le
         raise ValueError("q_lat must hold [B, q_len, n_h, 576]")
     if work.dim() != 2 or work.shape[1] != 4:
         raise ValueError("work must be [n_work, 4]")
+    if lists is not None and (lists.dim() != 1 or lists.shape[0] < 2):
+        raise ValueError("lists must be [n_lists + 1]")
     if o_lat.numel() != rows * n_h * D_C or lse.numel() != rows * n_h:
         raise ValueError("o_lat / lse must hold [B, q_len, n_h, 512] / [B, q_len, n_h]")
     if o_part is not None and (o_part.shape[-1] != D_C or o_part.numel() % (n_h * D_C) or
@@ -728,6 +731,8 @@ def mla_decode_paged_planned_fp8(q_lat, kv_cache, kv_scale, block_table, B, q_le
         int(kv_cache.shape[0]), int(kv_cache.shape[1]),
         _dev(block_table, "block_table", torch.int32), int(block_table.shape[1]), int(B),
         int(q_len), n_h, float(softmax_scale), _dev(work, "work", torch.int32),
-        int(work.shape[0]), _dev(o_part, "o_part", f32), _dev(lse_part, "lse_part", f32),
-        n_parts, _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32), _stream(stream))
+        int(work.shape[0]), _dev(lists, "lists", torch.int32),
+        int(lists.shape[0]) - 1 if lists is not None else 0, _dev(o_part, "o_part", f32),
+        _dev(lse_part, "lse_part", f32), n_parts, _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32),
+        _stream(stream))
     _check("mla_decode_paged_planned_fp8", st)

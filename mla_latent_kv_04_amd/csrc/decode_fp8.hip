@@ -342,13 +342,17 @@ hipError_t launch8(const void* q_lat, const void* cache, const float* kv_scale, 
 hipError_t launch_decode_fp8(const void* q_lat, const void* cache, const float* kv_scale,
                              int num_blocks, const int* table, int max_blocks,
                              const int* seq_lens, int B, int q_len, int n_h, float scale, int S,
-                             const int* work, int n_work, float* o_lat, float* lse,
-                             float* o_part, float* lse_part, int n_parts, hipStream_t stream) {
+                             const int* work, int n_work, const int* lists, int n_lists,
+                             float* o_lat, float* lse, float* o_part, float* lse_part,
+                             int n_parts, hipStream_t stream) {
+  if (n_h % 64 == 0)
+    return launch_decode_h64_fp8(q_lat, cache, kv_scale, num_blocks, table, max_blocks, seq_lens,
+                                 B, q_len, n_h, scale, S, work, n_work, lists, n_lists, o_lat,
+                                 lse, o_part, lse_part, n_parts, stream);
 #define MLA_FP8_ARGS q_lat, cache, kv_scale, num_blocks, table, max_blocks, seq_lens, B, q_len, \
                      n_h, scale, S, work, n_work, o_lat, lse, o_part, lse_part, n_parts, stream
   if (n_h == 16) return launch8<Cfg8<1, 4, 2>>(MLA_FP8_ARGS);
-  if (n_h == 32) return launch8<Cfg8<2, 2, 2>>(MLA_FP8_ARGS);
-  return launch8<Cfg8<4, 1, 1>>(MLA_FP8_ARGS);
+  return launch8<Cfg8<2, 2, 2>>(MLA_FP8_ARGS);
 #undef MLA_FP8_ARGS
 }
 

@@ -171,8 +171,8 @@ int32_t mla_decode_paged_fp8(const void* q_lat, const void* kv_cache, const floa
   const int64_t n_parts = num_splits > 1 ? (int64_t)B * q_len * num_splits : 0;
   return hip_status(mla::launch_decode_fp8(q_lat, kv_cache, kv_scale, num_blocks, block_table,
                                            max_blocks, seq_lens, B, q_len, n_h, softmax_scale,
-                                           num_splits, nullptr, 0, o_lat, lse, o_part, lse_part,
-                                           (int)n_parts, (hipStream_t)stream));
+                                           num_splits, nullptr, 0, nullptr, 0, o_lat, lse, o_part,
+                                           lse_part, (int)n_parts, (hipStream_t)stream));
 }
 
 int32_t mla_decode_paged_planned_fp8(const void* q_lat, const void* kv_cache,
@@ -180,10 +180,12 @@ int32_t mla_decode_paged_planned_fp8(const void* q_lat, const void* kv_cache,
                                      int32_t block_size, const int32_t* block_table,
                                      int32_t max_blocks, int32_t B, int32_t q_len, int32_t n_h,
                                      float softmax_scale, const int32_t* work, int32_t n_work,
-                                     float* o_part, float* lse_part, int32_t n_parts,
-                                     float* o_lat, float* lse, void* stream) {
+                                     const int32_t* lists, int32_t n_lists, float* o_part,
+                                     float* lse_part, int32_t n_parts, float* o_lat, float* lse,
+                                     void* stream) {
   if (B < 0 || q_len < 1 || num_blocks < 1 || max_blocks < 1 || block_size != MLA_BLOCK ||
-      !decode_heads_ok(n_h) || n_work < 0 || n_parts < 0 || !(softmax_scale > 0.0f))
+      !decode_heads_ok(n_h) || n_work < 0 || n_parts < 0 || !(softmax_scale > 0.0f) ||
+      (lists && n_lists < 1))
     return MLA_ERR_SHAPE;
   if ((int64_t)B * q_len > 0x7fffffffLL) return MLA_ERR_SHAPE;
   if (n_work == 0 || B == 0) return MLA_OK;
@@ -196,8 +198,8 @@ int32_t mla_decode_paged_planned_fp8(const void* q_lat, const void* kv_cache,
     return MLA_ERR_ALIGN;
   return hip_status(mla::launch_decode_fp8(q_lat, kv_cache, kv_scale, num_blocks, block_table,
                                            max_blocks, nullptr, B, q_len, n_h, softmax_scale, 1,
-                                           work, n_work, o_lat, lse, o_part, lse_part, n_parts,
-                                           (hipStream_t)stream));
+                                           work, n_work, lists, lists ? n_lists : 0, o_lat, lse,
+                                           o_part, lse_part, n_parts, (hipStream_t)stream));
 }
 
 int32_t mla_plan_decode(const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t block_size,

@@ -61,13 +61,21 @@ hipError_t launch_decode_h64(const void* q_lat, const void* cache, int num_block
                              const int* lists, int n_lists, float* o_lat, float* lse,
                              float* o_part, float* lse_part, int n_parts, hipStream_t stream);
 
-// FP8 E4M3 cache with per-row scales (decode_fp8.hip); queries bf16; any
-// head count the bf16 kernels take; one item per workgroup.
+// FP8 E4M3 cache with per-row scales; queries bf16; any head count the bf16
+// kernels take.  16 and 32 heads: decode_fp8.hip, one item per workgroup;
+// multiples of 64: the FP8 form of decode_h64.hip (lists as there).
 hipError_t launch_decode_fp8(const void* q_lat, const void* cache, const float* kv_scale,
                              int num_blocks, const int* table, int max_blocks,
                              const int* seq_lens, int B, int q_len, int n_h, float scale, int S,
-                             const int* work, int n_work, float* o_lat, float* lse,
-                             float* o_part, float* lse_part, int n_parts, hipStream_t stream);
+                             const int* work, int n_work, const int* lists, int n_lists,
+                             float* o_lat, float* lse, float* o_part, float* lse_part,
+                             int n_parts, hipStream_t stream);
+hipError_t launch_decode_h64_fp8(const void* q_lat, const void* cache, const float* kv_scale,
+                                 int num_blocks, const int* table, int max_blocks,
+                                 const int* seq_lens, int B, int q_len, int n_h, float scale, int S,
+                                 const int* work, int n_work, const int* lists, int n_lists,
+                                 float* o_lat, float* lse, float* o_part, float* lse_part,
+                                 int n_parts, hipStream_t stream);
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int B, int S, int q_len,
                           int n_h, float* o_lat, float* lse, hipStream_t stream);

@@ -224,7 +224,8 @@ def _attend_planned(dp: DeviceProblem, stream=None):
     if dp.kv_scale is not None:
         mla.mla_decode_paged_planned_fp8(dp.q_lat, dp.kv_cache, dp.kv_scale, dp.block_table, dp.B,
                                          dp.q_len, softmax_scale(), dp.work, dp.o_lat, dp.lse,
-                                         o_part=dp.o_part, lse_part=dp.lse_part, stream=stream)
+                                         o_part=dp.o_part, lse_part=dp.lse_part, lists=dp.lists,
+                                         stream=stream)
         return
     mla.mla_decode_paged_planned(dp.q_lat, dp.kv_cache, dp.block_table, dp.B, dp.q_len,
                                  softmax_scale(), dp.work, dp.o_lat, dp.lse,

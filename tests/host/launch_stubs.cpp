@@ -40,8 +40,8 @@ hipError_t launch_decode_h64(const void*, const void*, int, const int*, int, con
   return counted();
 }
 hipError_t launch_decode_fp8(const void*, const void*, const float*, int, const int*, int,
-                             const int*, int, int, int, float, int, const int*, int, float*, float*,
-                             float*, float*, int, hipStream_t) {
+                             const int*, int, int, int, float, int, const int*, int, const int*,
+                             int, float*, float*, float*, float*, int, hipStream_t) {
   return counted();
 }
 hipError_t launch_combine(const float*, const float*, int, int, int, int, float*, float*,

@@ -116,8 +116,10 @@ void entry_points() {
                               FF, nullptr), MLA_OK);
   EXPECT(mla_decode_paged_planned(F, F, 4, 64, FI, 4, 2, 1, 64, 1, 0.07f, FI, 5, FI, 2, FF, FF, 3,
                                   FF, FF, nullptr), MLA_OK);
-  EXPECT(mla_decode_paged_planned_fp8(F, F, FF, 4, 64, FI, 4, 2, 1, 32, 0.07f, FI, 5, FF, FF, 3,
-                                      FF, FF, nullptr), MLA_OK);
+  EXPECT(mla_decode_paged_planned_fp8(F, F, FF, 4, 64, FI, 4, 2, 1, 32, 0.07f, FI, 5, nullptr, 0,
+                                      FF, FF, 3, FF, FF, nullptr), MLA_OK);
+  EXPECT(mla_decode_paged_planned_fp8(F, F, FF, 4, 64, FI, 4, 2, 1, 128, 0.07f, FI, 5, FI, 0,
+                                      FF, FF, 3, FF, FF, nullptr), MLA_ERR_SHAPE);
   EXPECT(mla_splitkv_combine(FF, FF, 2, 3, 1, 16, FF, FF, nullptr), MLA_OK);
   EXPECT(mla_combine_planned(FF, FF, FI, 2, 16, FF, FF, nullptr), MLA_OK);
   EXPECT(mla_out_proj(FF, F, 4, 16, 1, FF, nullptr), MLA_OK);

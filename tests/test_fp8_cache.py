@@ -173,6 +173,31 @@ def test_fp8_step_full_size_lite_every_output():
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.timeout(900)
+def test_fp8_step_full_size_v2_every_output():
+    """The V2 decode workload (B=128, 128 heads, L ~ U[1024, 8192]) with the
+    FP8 cache through the two-role 64-head kernel, balanced plan with lists:
+    every output against the oracle's attention over the dequantised rows."""
+    import torch
+    prob = make_problem(WORKLOADS[F3])
+    say("fp8 full-size v2 step")
+    dp = pipeline.upload(prob, num_splits=0, cache="fp8")
+    pipeline.step(dp)
+    torch.cuda.synchronize()
+    out, lse = to_np(dp.out), to_np(dp.lse)
+    host, q_lat = _host_cache(dp), to_np(dp.q_lat)
+    refs, lrefs = [], []
+    for b in range(prob.wl.B):
+        o_lat, l = _oracle_on_gpu_rows(dp, host, q_lat, b)
+        refs.append(orc.out_projection(o_lat, prob.w_uv))
+        lrefs.append(l)
+    ref, lref = np.concatenate(refs), np.concatenate(lrefs)
+    err = rel_err(out, ref)
+    print(f"[fp8] full-size v2: max|err|/rms = {err:.3e} over {out.size} outputs", flush=True)
+    assert err <= TOL["bf16"]
+    assert np.max(np.abs(lse - lref)) <= TOL["bf16"] * max(1.0, float(np.abs(lref).max()))
+
+
 def test_fp8_quantisation_error_against_the_unquantised_cache():
     """What the format costs: the same step with the bf16 cache and with the
     FP8 cache, each against the unquantised oracle.  The FP8 step's error is
