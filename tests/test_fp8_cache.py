@@ -227,3 +227,89 @@ def test_fp8_quantisation_error_against_the_unquantised_cache():
     print(f"[fp8] rms err/rms: bf16 cache {e_native:.3e}, fp8 cache {e_fp8:.3e}", flush=True)
     assert e_native <= 4e-3
     assert 1e-2 <= e_fp8 <= 5e-2
+
+
+@pytest.mark.parametrize("wl,n_h,S", [(F3, 128, 0), (F3, 128, 1), (F2, 16, 1)],
+                         ids=["h128-planned", "h128-S1", "h16-S1"])
+def test_fp8_rising_scores_force_running_max_updates(wl, n_h, S):
+    """Cached rows scaled up tile by tile: the running maximum keeps moving, so
+    the rescale of the accumulators and (in the 64-head kernel) the rewrite of
+    P and of the normaliser the score waves keep run on most tiles."""
+    import torch
+    from mla_latent_kv_04_amd.workloads import round_to_bf16
+    prob = small(wl, B=2, ctx=[1500, 3000], n_h=n_h)
+    pos = np.concatenate([np.arange(int(L)) for L in prob.seq_lens])
+    f = (1.0 + pos // 32)[:, None]
+    prob.c_kv = round_to_bf16(prob.c_kv * f)
+    prob.k_r = round_to_bf16(prob.k_r * f)
+    say(f"fp8 rising scores {wl} S={S}")
+    dp = pipeline.upload(prob, num_splits=S, cache="fp8")
+    pipeline.append(dp)
+    from mla_latent_kv_04_amd import _binding as mla
+    mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE)
+    pipeline.decode(dp)
+    torch.cuda.synchronize()
+    o_lat, lse = to_np(dp.o_lat), to_np(dp.lse)
+    host, q_lat = _host_cache(dp), to_np(dp.q_lat)
+    for b in range(2):
+        ref, lref = _oracle_on_gpu_rows(dp, host, q_lat, b)
+        assert rel_err(o_lat[b:b + 1], ref) <= TOL["bf16"], b
+        assert np.max(np.abs(lse[b:b + 1] - lref)) <= TOL["bf16"] * max(1.0, np.abs(lref).max())
+
+
+@pytest.mark.timeout(600)
+def test_fp8_long_context_sampled():
+    """The 128K workload with the FP8 cache (items longer than one staged
+    chunk of block ids): sampled heads of every row against the oracle over
+    the dequantised rows."""
+    import torch
+    prob = make_problem(WORKLOADS[F4])
+    say("fp8 128K")
+    dp = pipeline.upload(prob, num_splits=0, cache="fp8")
+    pipeline.step(dp)
+    torch.cuda.synchronize()
+    out = to_np(dp.out)
+    host, q_lat = _host_cache(dp), to_np(dp.q_lat)
+    heads = [0, 63, 64, 127]
+    for b in range(prob.wl.B):
+        L = int(prob.seq_lens[b])
+        codes, scales = _cache_rows(dp, host, b, L)
+        deq = orc.dequantize_rows(codes, scales, D_C)
+        o_lat, _ = orc.latent_attention(q_lat[b:b + 1][:, heads], deq, [L], softmax_scale(), D_C)
+        ref = orc.out_projection(o_lat, prob.w_uv[heads])
+        assert rel_err(out[b:b + 1][:, heads], ref) <= TOL["bf16"], b
+
+
+def test_fp8_append_with_a_yarn_table():
+    """The quantising append rotates with a given RoPE table (YaRN's): codes
+    and scales equal the oracle's for the same table."""
+    import torch
+    from mla_latent_kv_04_amd import _binding as mla
+    from mla_latent_kv_04_amd.workloads import round_to_bf16
+    rng = np.random.default_rng(61)
+    n = 130
+    pos = np.sort(rng.choice(163840, n, replace=False)).astype(np.int32)
+    used = np.unique(pos // BLOCK)
+    table = np.full((1, 163840 // BLOCK), -1, np.int32)
+    table[0, used] = np.arange(len(used))
+    c = round_to_bf16(rng.standard_normal((n, D_C)).astype(np.float32))
+    kr = round_to_bf16(rng.standard_normal((n, 64)).astype(np.float32))
+    th = mla.mla_rope_theta(ROPE_BASE, 40.0, 1.0, 32.0, 4096)
+    cache = torch.full((len(used), BLOCK, 576), 0xFF, dtype=torch.uint8, device="cuda")
+    scales = torch.full((len(used), BLOCK, 2), float("nan"), dtype=torch.float32, device="cuda")
+    say("fp8 append yarn")
+    bf = torch.bfloat16
+    mla.mla_kv_append_fp8(cache, scales, torch.from_numpy(table).cuda(),
+                          torch.from_numpy(c).to(bf).cuda(), torch.from_numpy(kr).to(bf).cuda(),
+                          torch.zeros(n, dtype=torch.int32, device="cuda"),
+                          torch.from_numpy(pos).cuda(), ROPE_BASE, rope_theta=th)
+    torch.cuda.synchronize()
+    blk, row = table[0, pos // BLOCK], pos % BLOCK
+    gc, gs = cache.cpu().numpy()[blk, row], scales.cpu().numpy()[blk, row]
+    want_c, want_s = orc.kv_cache_rows_fp8(c.astype(np.float64), kr.astype(np.float64), pos,
+                                           ROPE_BASE, orc.yarn_theta(64, ROPE_BASE, 40, 1, 32, 4096))
+    np.testing.assert_array_equal(gc[:, :D_C], want_c[:, :D_C])
+    np.testing.assert_array_equal(gs[:, 0], want_s[:, 0])
+    # RoPE part: exact unless a float64 rotation lands on a float32 tie (none
+    # expected among 130 rows)
+    assert np.sum(np.any(gc[:, D_C:] != want_c[:, D_C:], axis=1)) <= 1
