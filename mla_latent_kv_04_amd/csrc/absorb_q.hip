@@ -5,19 +5,30 @@
 // the irregular6612.github.io DeepSeek-V2 notes, §2.1.2).
 //
 // Per head i this is the GEMM q_lat^T[c, t] = sum_d W^UK_i[d, c] q_nope[t, i, d]
-// with M = 512 (latent c), N = T (rows), K = 128 (d).  One workgroup of four
-// waves owns one head, 64 latent columns and 128 rows; the 128 x 64 weight
-// tile is staged in LDS once and read as the MFMA A operand (rows c, reduced
-// d) with the transposing LDS read, since W^UK is stored with c contiguous.
-// The query fragments (reduced d contiguous) come straight from memory.
+// with M = 512 (latent c), N = T (rows), K = 128 (d).  A workgroup of four
+// waves multiplies 128 rows of one head against 64-column tiles of the
+// weight: each 128 x 64 tile is staged in LDS and read as the MFMA A operand
+// (rows c, reduced d) with the transposing LDS read, since W^UK is stored with
+// c contiguous.  The query fragments (reduced d contiguous) come straight from
+// memory into registers.
 //
 // The A rows of the four 16-column MFMA blocks are permuted so that the
 // output lands row-contiguous: block cb's row m is latent column
 // 16 (m >> 2) + 4 cb + (m & 3), so after the four blocks a lane holds 16
 // consecutive columns of one query row and writes them with full-width
-// stores (four lanes cover a row's 64 columns).  The RoPE half of q_lat is
-// shared out over the eight column-chunk workgroups of a head, 4 of the 32
-// rotation pairs each.
+// stores (four lanes cover a row's 64 columns).
+//
+// bf16 (the decode and prefill path): a workgroup owns CPW consecutive tiles
+// of its head.  It loads the query fragments once for all of them and
+// streams the tiles through two LDS buffers, with the next tiles already in
+// flight in registers while one is multiplied and stored, so each
+// workgroup's stores overlap its next loads; CPW grows with the number of
+// (head, 128-row) units, from 1 for a few heads to 4 for long prefill
+// chunks (where it cuts the query re-reads fourfold).  The RoPE half goes by
+// whole rows: each workgroup rotates all 32 pairs of its share of the rows,
+// so every 128-byte RoPE section is read and written by one workgroup.
+// fp32 (the reference-precision path): one tile per workgroup, RoPE in
+// float64, 4 of the 32 pairs per column tile.
 #include <cmath>
 
 #include "mla_common.h"
@@ -27,7 +38,7 @@ namespace mla {
 
 namespace {
 
-constexpr int CCH = 64;        // latent columns per workgroup
+constexpr int CCH = 64;        // latent columns per weight tile
 
 // RoPE frequencies in revolutions per position, theta_k / (2 pi), computed
 // on the host in float64 from the pair frequencies theta_k.
@@ -35,7 +46,7 @@ struct RopeRev {
   double r[D_R / 2];
 };
 constexpr int TCH = 128;       // rows per workgroup (4 waves x 2 blocks of 16)
-constexpr int KPW = (D_R / 2) / (D_C / CCH);   // RoPE pairs per workgroup
+constexpr int KPW = (D_R / 2) / (D_C / CCH);   // RoPE pairs per fp32 workgroup
 
 template <class E> struct AbsorbLds;
 // bf16: a 136-byte row pitch puts the four rows of a transposing read on
@@ -93,13 +104,11 @@ __device__ __forceinline__ void store16<F32>(float* dst, const float (&v)[16]) {
   for (int i = 0; i < 4; ++i) d[i] = float4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
 }
 
-template <class E>
-__global__ void __launch_bounds__(256) absorb_q_kernel(
-    const typename E::storage* __restrict__ q_nope, const typename E::storage* __restrict__ q_rope,
-    const typename E::storage* __restrict__ w_uk, const int* __restrict__ q_pos, int T, int n_h,
-    RopeFreq rf, RopeRev rev, typename E::storage* __restrict__ q_lat) {
-  using T_ = typename E::storage;
-  constexpr int S = AbsorbLds<E>::stride;
+__global__ void __launch_bounds__(256) absorb_q_f32_kernel(
+    const float* __restrict__ q_nope, const float* __restrict__ q_rope,
+    const float* __restrict__ w_uk, const int* __restrict__ q_pos, int T, int n_h, RopeFreq rf,
+    float* __restrict__ q_lat) {
+  constexpr int S = AbsorbLds<F32>::stride;
   __shared__ __attribute__((aligned(16))) char lds[D_H * S];
   const int h = blockIdx.x;
   const int c0 = blockIdx.y * CCH;
@@ -108,67 +117,44 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
 
   // Query fragments (B operand): lane holds row t = tb*16 + r16, d = ks*32 + 8g + j
   // (issued first, so that they land while the weight tile is staged).
-  typename E::frag qf[2][4];
+  F32::frag qf[2][4];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     const int t = t0 + wave * 32 + tb * 16 + r16;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (t < T) {
-        qf[tb][ks] = E::load8(q_nope + ((long)t * n_h + h) * D_H + ks * 32 + 8 * g);
+        qf[tb][ks] = F32::load8(q_nope + ((long)t * n_h + h) * D_H + ks * 32 + 8 * g);
       } else {
         float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        qf[tb][ks] = E::from8(z);
+        qf[tb][ks] = F32::from8(z);
       }
     }
   }
-  // bf16 RoPE inputs (two rotation pairs per thread), loaded with the
-  // fragments and rotated after the product, so their latency is hidden
-  constexpr int RPT = TCH * KPW / 256;
-  static_assert(TCH * KPW % 256 == 0, "rotation pairs split evenly");
-  uint32_t rp[RPT];
-  int rpos[RPT];
-  if constexpr (E::bytes == 2) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int e = threadIdx.x + 256 * i;
-      const int t = t0 + e / KPW, k = blockIdx.y * KPW + e % KPW;
-      rp[i] = 0;
-      rpos[i] = 0;
-      if (t < T) {
-        rp[i] = *reinterpret_cast<const uint32_t*>(q_rope + ((long)t * n_h + h) * D_R + 2 * k);
-        rpos[i] = q_pos[t];
-      }
-    }
-  }
-  // Stage W^UK_h[0:128, c0:c0+64] (16-byte pieces, written as two halves:
-  // the bf16 row pitch is a multiple of 8 bytes only).
-  constexpr int PER16 = 16 / E::bytes;
-  constexpr int PIECES_PER_ROW = CCH / PER16;
-  const T_* wsrc = w_uk + (long)h * D_H * D_C + c0;
+  // Stage W^UK_h[0:128, c0:c0+64] (16-byte pieces).
+  constexpr int PIECES_PER_ROW = CCH / 4;
+  const float* wsrc = w_uk + (long)h * D_H * D_C + c0;
   constexpr int NP = D_H * PIECES_PER_ROW / 256;   // pieces per thread
   static_assert(D_H * PIECES_PER_ROW % 256 == 0, "pieces split evenly");
   uint4 wv[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int p = i * 256 + threadIdx.x, d = p / PIECES_PER_ROW, q = p % PIECES_PER_ROW;
-    wv[i] = *reinterpret_cast<const uint4*>(wsrc + (long)d * D_C + q * PER16);
+    wv[i] = *reinterpret_cast<const uint4*>(wsrc + (long)d * D_C + q * 4);
   }
 
-  // Decoupled RoPE query, this column chunk's 4 of the 32 rotation pairs.
-  if constexpr (E::bytes == 4) {
-    // fp32: float64 angles and rotation (runs while the loads above are in flight)
-    for (int e = threadIdx.x; e < TCH * KPW; e += 256) {
-      const int t = t0 + e / KPW, k = blockIdx.y * KPW + e % KPW;
-      if (t >= T) break;
-      const T_* src = q_rope + ((long)t * n_h + h) * D_R;
-      T_* dst = q_lat + ((long)t * n_h + h) * ROW + D_C;
-      double c, s;
-      rope_cs(q_pos[t], rf.theta[k], c, s);
-      double x = E::to_f32(src[2 * k]), y = E::to_f32(src[2 * k + 1]);
-      dst[2 * k] = E::from_f32((float)(x * c - y * s));
-      dst[2 * k + 1] = E::from_f32((float)(x * s + y * c));
-    }
+  // Decoupled RoPE query, this column chunk's 4 of the 32 rotation pairs:
+  // float64 angles and rotation (runs while the loads above are in flight).
+  for (int e = threadIdx.x; e < TCH * KPW; e += 256) {
+    const int t = t0 + e / KPW, k = blockIdx.y * KPW + e % KPW;
+    if (t >= T) break;
+    const float* src = q_rope + ((long)t * n_h + h) * D_R;
+    float* dst = q_lat + ((long)t * n_h + h) * ROW + D_C;
+    double c, s;
+    rope_cs(q_pos[t], rf.theta[k], c, s);
+    const double x = src[2 * k], y = src[2 * k + 1];
+    dst[2 * k] = (float)(x * c - y * s);
+    dst[2 * k + 1] = (float)(x * s + y * c);
   }
 
 #pragma unroll
@@ -187,9 +173,9 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
     acc[1][cb] = f32x4_t{0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      typename E::frag wf = load_wt_frag<E>(lds, ks * 32 + 8 * g, cb);
-      E::mma(acc[0][cb], wf, qf[0][ks]);
-      E::mma(acc[1][cb], wf, qf[1][ks]);
+      const F32::frag wf = load_wt_frag<F32>(lds, ks * 32 + 8 * g, cb);
+      F32::mma(acc[0][cb], wf, qf[0][ks]);
+      F32::mma(acc[1][cb], wf, qf[1][ks]);
     }
   }
   // D[m][t] of block cb: lane holds t = r16 (+16 tb) and m = 4g + i, i.e.
@@ -203,27 +189,133 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
       for (int cb = 0; cb < CCH / 16; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[4 * cb + i] = acc[tb][cb][i];
-      store16<E>(q_lat + ((long)t * n_h + h) * ROW + c0 + 16 * g, v);
+      store16<F32>(q_lat + ((long)t * n_h + h) * ROW + c0 + 16 * g, v);
     }
   }
-  if constexpr (E::bytes == 2) {
-    // the angle is reduced exactly in float64 (whole turns dropped), then sine
-    // and cosine in float32, far below bf16's rounding
+}
+
+// bf16: workgroup (h, gy, z) owns the CPW consecutive 64-column tiles of
+// head h that start at column 64 CPW gy, for rows 128 z .. 128 z + 127, and
+// the RoPE part of rows 128 z + RROWS gy .. + RROWS - 1 (RROWS = 16 CPW).
+// Tile c + PF is loaded into registers while tile c is multiplied; the LDS
+// holds two tiles.
+template <int CPW, int PF>
+__global__ void __launch_bounds__(256) absorb_q_bf16_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ w_uk, const int* __restrict__ q_pos, int T, int n_h, RopeRev rev,
+    uint16_t* __restrict__ q_lat) {
+  constexpr int S = AbsorbLds<BF16>::stride;
+  constexpr int NG = (D_C / CCH) / CPW;   // column groups per head
+  __shared__ __attribute__((aligned(16))) char lds[2][D_H * S];
+  constexpr int TBW = TCH / 64;           // 16-row blocks per wave
+  const int h = blockIdx.x, gy = blockIdx.y, t0 = blockIdx.z * TCH;
+  const int tid = threadIdx.x;
+  const int lane = lane_id(), wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+
+  // query fragments (B operand): row t = t0 + 32 wave + 16 tb + r16, d = 32 ks + 8 g + j
+  BF16::frag qf[TBW][4];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int e = threadIdx.x + 256 * i;
-      const int t = t0 + e / KPW, k = blockIdx.y * KPW + e % KPW;
-      if (t >= T) continue;
-      double turns = (double)rpos[i] * rev.r[k];
+  for (int tb = 0; tb < TBW; ++tb) {
+    const int t = t0 + wave * 16 * TBW + tb * 16 + r16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (t < T) {
+        qf[tb][ks] = BF16::load8(q_nope + ((long)t * n_h + h) * D_H + ks * 32 + 8 * g);
+      } else {
+        float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        qf[tb][ks] = BF16::from8(z);
+      }
+    }
+  }
+  // RoPE inputs: rows t0 + RROWS gy + 16 i + (tid >> 4), pairs 2 (tid & 15) and + 1
+  constexpr int RROWS = TCH / NG, RPASS = RROWS / 16;
+  static_assert(RROWS % 16 == 0, "RoPE rows split evenly");
+  const int rk = 2 * (tid & 15);
+  uint2 rp[RPASS];
+  int rpos[RPASS];
+#pragma unroll
+  for (int i = 0; i < RPASS; ++i) {
+    const int t = t0 + RROWS * gy + 16 * i + (tid >> 4);
+    rp[i] = uint2{0, 0};
+    rpos[i] = 0;
+    if (t < T) {
+      rp[i] = *reinterpret_cast<const uint2*>(q_rope + ((long)t * n_h + h) * D_R + 2 * rk);
+      rpos[i] = q_pos[t];
+    }
+  }
+  // weight tile c: W^UK_h[0:128, 64 (CPW gy + c) ..], four 16-byte pieces per thread
+  const uint16_t* wsrc = w_uk + (long)h * D_H * D_C + CPW * gy * CCH;
+  auto load_w = [&](int c, uint4 (&wv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = i * 256 + tid, d = p >> 3, q = p & 7;
+      wv[i] = *reinterpret_cast<const uint4*>(wsrc + (long)d * D_C + c * CCH + q * 8);
+    }
+  };
+  auto stage_w = [&](char* buf, const uint4 (&wv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = i * 256 + tid, d = p >> 3, q = p & 7;
+      uint2* dst = reinterpret_cast<uint2*>(buf + d * S + q * 16);
+      dst[0] = uint2{wv[i].x, wv[i].y};
+      dst[1] = uint2{wv[i].z, wv[i].w};
+    }
+  };
+  uint4 wv[PF][4];
+#pragma unroll
+  for (int c = 0; c < PF && c < CPW; ++c) load_w(c, wv[c]);
+
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    char* buf = lds[c & 1];
+    stage_w(buf, wv[c % PF]);
+    if (c + PF < CPW) load_w(c + PF, wv[c % PF]);
+    __syncthreads();
+    f32x4_t acc[TBW][CCH / 16];
+#pragma unroll
+    for (int cb = 0; cb < CCH / 16; ++cb) {
+#pragma unroll
+      for (int tb = 0; tb < TBW; ++tb) acc[tb][cb] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const BF16::frag wf = load_wt_frag<BF16>(buf, ks * 32 + 8 * g, cb);
+#pragma unroll
+        for (int tb = 0; tb < TBW; ++tb) BF16::mma(acc[tb][cb], wf, qf[tb][ks]);
+      }
+    }
+    // lane holds row t = ... + r16 and columns 16 g .. 16 g + 15 of the chunk
+#pragma unroll
+    for (int tb = 0; tb < TBW; ++tb) {
+      const int t = t0 + wave * 16 * TBW + tb * 16 + r16;
+      if (t < T) {
+        float v[16];
+#pragma unroll
+        for (int cb = 0; cb < CCH / 16; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[4 * cb + i] = acc[tb][cb][i];
+        store16<BF16>(q_lat + ((long)t * n_h + h) * ROW + (CPW * gy + c) * CCH + 16 * g, v);
+      }
+    }
+  }
+  // the angle is reduced exactly in float64 (whole turns dropped), then sine
+  // and cosine in float32, far below bf16's rounding
+#pragma unroll
+  for (int i = 0; i < RPASS; ++i) {
+    const int t = t0 + RROWS * gy + 16 * i + (tid >> 4);
+    if (t >= T) continue;
+    uint32_t out[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      double turns = (double)rpos[i] * rev.r[rk + j];
       turns -= rint(turns);
       float sf, cf;
       sincosf((float)(turns * 6.283185307179586), &sf, &cf);
-      const float x = bf16_to_f32((uint16_t)(rp[i] & 0xFFFFu)), y = bf16_to_f32((uint16_t)(rp[i] >> 16));
-      *reinterpret_cast<uint32_t*>(q_lat + ((long)t * n_h + h) * ROW + D_C + 2 * k) =
-          pack_bf16x2(x * cf - y * sf, x * sf + y * cf);
+      const uint32_t w = j == 0 ? rp[i].x : rp[i].y;
+      const float x = bf16_to_f32((uint16_t)(w & 0xFFFFu)), y = bf16_to_f32((uint16_t)(w >> 16));
+      out[j] = pack_bf16x2(x * cf - y * sf, x * sf + y * cf);
     }
+    *reinterpret_cast<uint2*>(q_lat + ((long)t * n_h + h) * ROW + D_C + 2 * rk) = uint2{out[0], out[1]};
   }
-
 }
 
 }  // namespace
@@ -231,18 +323,34 @@ __global__ void __launch_bounds__(256) absorb_q_kernel(
 hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
                            const int* q_pos, int T, int n_h, int dtype, const RopeFreq& rf,
                            void* q_lat, hipStream_t stream) {
-  dim3 grid(n_h, D_C / CCH, (T + TCH - 1) / TCH), block(256);
+  const int nz = (T + TCH - 1) / TCH;
+  if (dtype != 1) {
+    hipLaunchKernelGGL(absorb_q_f32_kernel, dim3(n_h, D_C / CCH, nz), dim3(256), 0, stream,
+                       (const float*)q_nope, (const float*)q_rope, (const float*)w_uk, q_pos, T,
+                       n_h, rf, (float*)q_lat);
+    return hipGetLastError();
+  }
   RopeRev rev;
   for (int k = 0; k < D_R / 2; ++k)
     rev.r[k] = rf.theta[k] / 6.283185307179586;
-  if (dtype == 1)
-    hipLaunchKernelGGL(absorb_q_kernel<BF16>, grid, block, 0, stream, (const uint16_t*)q_nope,
-                       (const uint16_t*)q_rope, (const uint16_t*)w_uk, q_pos, T, n_h,
-                       rf, rev, (uint16_t*)q_lat);
+  auto* q = (const uint16_t*)q_nope;
+  auto* r = (const uint16_t*)q_rope;
+  auto* w = (const uint16_t*)w_uk;
+  auto* o = (uint16_t*)q_lat;
+  // tiles per workgroup by the number of (head, 128-row) units: measured on
+  // 16 x 64, 128 x 128 and 128 x 2048 (heads x rows), one tile per
+  // workgroup keeps a few heads spread over the chip; four, with three tiles
+  // in flight, suits long prefill chunks
+  const int units = n_h * nz;
+  if (units >= 1024)
+    hipLaunchKernelGGL((absorb_q_bf16_kernel<4, 3>), dim3(n_h, 2, nz), dim3(256), 0, stream, q, r,
+                       w, q_pos, T, n_h, rev, o);
+  else if (units >= 64)
+    hipLaunchKernelGGL((absorb_q_bf16_kernel<2, 2>), dim3(n_h, 4, nz), dim3(256), 0, stream, q, r,
+                       w, q_pos, T, n_h, rev, o);
   else
-    hipLaunchKernelGGL(absorb_q_kernel<F32>, grid, block, 0, stream, (const float*)q_nope,
-                       (const float*)q_rope, (const float*)w_uk, q_pos, T, n_h, rf, rev,
-                       (float*)q_lat);
+    hipLaunchKernelGGL((absorb_q_bf16_kernel<1, 2>), dim3(n_h, 8, nz), dim3(256), 0, stream, q, r,
+                       w, q_pos, T, n_h, rev, o);
   return hipGetLastError();
 }
 

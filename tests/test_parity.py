@@ -123,10 +123,18 @@ def test_kv_append_places_rows_exactly(dtype_wl):
     assert np.isnan(cache[~seen]).all()
 
 
-@pytest.mark.parametrize("wl,n_h", [(F1, 16), (F3, 128), (F5, 128)])
-def test_absorb_q_matches_oracle(wl, n_h):
-    prob = small(wl, B=3, ctx=[40, 41, 42], n_h=n_h) if wl != F5 else small(wl, ctx=200, q_len=150)
-    say(f"absorb {wl}")
+ABSORB_CASES = [(F1, dict(B=3, ctx=[40, 41, 42], n_h=16)),
+                (F3, dict(B=3, ctx=[40, 41, 42], n_h=16)),     # bf16, one weight tile per workgroup
+                (F3, dict(B=3, ctx=[40, 41, 42], n_h=128)),    # two tiles per workgroup
+                (F5, dict(ctx=200, q_len=150)),                # two tiles, a ragged 128-row block
+                (F5, dict(ctx=1200, q_len=1100))]              # four tiles, 9 row blocks
+
+
+@pytest.mark.parametrize("wl,kw", ABSORB_CASES, ids=[f"{w}-T{k.get('q_len', k.get('B'))}-h{k.get('n_h', 128)}"
+                                                     for w, k in ABSORB_CASES])
+def test_absorb_q_matches_oracle(wl, kw):
+    prob = small(wl, **kw)
+    say(f"absorb {wl} {kw}")
     dp = run_step(prob)
     got = to_np(dp.q_lat)
     ref = orc.absorb_query(prob.q_nope, prob.q_rope, prob.w_uk, prob.q_pos, ROPE_BASE)
