@@ -33,6 +33,7 @@ PRODUCER_EPS = 1e-6           # RMSNorm epsilon of the latent and query norms
 # sources of the attention kernels; the committed HBM-traffic record is only
 # used while these are unchanged
 DECODE_SOURCES = ["mla_latent_kv_04_amd/csrc/decode.hip", "mla_latent_kv_04_amd/csrc/decode_h64.hip",
+                  "mla_latent_kv_04_amd/csrc/decode_h64_fp8.hip", "mla_latent_kv_04_amd/csrc/decode_h64_common.h",
                   "mla_latent_kv_04_amd/csrc/decode_fp8.hip",
                   "mla_latent_kv_04_amd/csrc/mla_common.h", "mla_latent_kv_04_amd/csrc/mla_api.cpp"]
 

@@ -27,13 +27,16 @@ COMMON = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 # Keep compiler-generated MFMA accumulators in the VGPR form; the register
-# allocator then places long-lived operands in AGPRs.  decode_h64.hip is the
-# exception: its value waves keep their accumulators in AGPRs (AGPR form).
+# allocator then places long-lived operands in AGPRs.  The two-role kernels
+# (decode_h64.hip, decode_h64_fp8.hip) are the exception: their value waves
+# keep their accumulators in AGPRs (AGPR form).
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-SOURCES = ["kv_append.hip", "absorb_q.hip", "decode.hip", "decode_h64.hip", "decode_fp8.hip",
+SOURCES = ["kv_append.hip", "absorb_q.hip", "decode.hip", "decode_h64.hip", "decode_h64_fp8.hip",
+           "decode_fp8.hip",
            "combine.hip", "out_proj.hip", "produce.hip", "prefill_mha.hip", "noalloc.hip",
            "mla_api.cpp", "produce_api.cpp"]
-EXTRA = {src: VGPR_FORM for src in SOURCES if src.endswith(".hip") and src != "decode_h64.hip"}
+EXTRA = {src: VGPR_FORM for src in SOURCES
+         if src.endswith(".hip") and src not in ("decode_h64.hip", "decode_h64_fp8.hip")}
 
 
 def _hipcc() -> str:

@@ -63,7 +63,8 @@ hipError_t launch_decode_h64(const void* q_lat, const void* cache, int num_block
 
 // FP8 E4M3 cache with per-row scales; queries bf16; any head count the bf16
 // kernels take.  16 and 32 heads: decode_fp8.hip, one item per workgroup;
-// multiples of 64: the FP8 form of decode_h64.hip (lists as there).
+// multiples of 64: decode_h64_fp8.hip, the two-role design with 64-token tiles
+// (lists as there).
 hipError_t launch_decode_fp8(const void* q_lat, const void* cache, const float* kv_scale,
                              int num_blocks, const int* table, int max_blocks,
                              const int* seq_lens, int B, int q_len, int n_h, float scale, int S,
