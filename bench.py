@@ -42,9 +42,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha() -> str:
+PREFILL_MHA_SOURCES = ["mla_latent_kv_04_amd/csrc/prefill_mha.hip",
+                       "mla_latent_kv_04_amd/csrc/mla_common.h",
+                       "mla_latent_kv_04_amd/csrc/produce_api.cpp"]
+TRAFFIC_SOURCES = {"decode": DECODE_SOURCES, "prefill_mha": PREFILL_MHA_SOURCES}
+
+
+def source_sha(kind: str = "decode") -> str:
     h = hashlib.sha256()
-    for p in DECODE_SOURCES:
+    for p in TRAFFIC_SOURCES[kind]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -74,16 +80,18 @@ def algorithmic_work(prob, fp8=False):
     return by, fl
 
 
-def load_traffic(workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source (else None).  workload: the workload's
-    name, with "_fp8" for the FP8 cache."""
-    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
+def load_traffic(workload: str, kind: str = "decode"):
+    """HBM bytes per launch of the timed attention kernel from committed
+    rocprofv3 counter runs, if they were taken on the current source of that
+    kernel (else None).  workload: the workload's name, with "_fp8" for the
+    FP8 cache; kind: "decode" (the absorbed attention kernels) or
+    "prefill_mha" (the non-absorbed prefill kernel)."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha") != source_sha():
+    if rec.get("source_sha") != source_sha(kind):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -499,7 +507,8 @@ def main():
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if wl.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     gbs = by / (dec_ms * 1e-3) / 1e9
     tflops = fl / (dec_ms * 1e-3) / 1e12
-    traffic = load_traffic(wl.name + ("_fp8" if fp8 else ""))
+    traffic = (load_traffic(wl.name, "prefill_mha") if non_absorbed
+               else load_traffic(wl.name + ("_fp8" if fp8 else "")))
     if compute_bound:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": mfma_peak,
                 "unit": "TFLOP/s", "frac": round(tflops / mfma_peak, 4), "traffic": traffic}
@@ -566,7 +575,7 @@ def main():
                              "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                              "mfma_tflops": round(tflops, 1),
                              "mfma_frac": round(tflops / mfma_peak, 4),
-                             "source_sha": source_sha()},
+                             "source_sha": source_sha("prefill_mha" if non_absorbed else "decode")},
         "cpu_baseline": cpu,
     }
     if producers is not None:

@@ -81,3 +81,14 @@ def test_traffic_record_applies_only_to_the_sources_it_was_taken_on():
         assert got is None
     assert bench.load_traffic("v2lite_f32_L256") is None       # no record
     assert rec["hbm_bytes_per_launch"] >= rec["algorithmic_bytes_per_launch"] * 0.9
+    # the non-absorbed prefill times another kernel: its own record, keyed on
+    # that kernel's sources
+    wl = "v2_bf16_prefill_6144+2048"
+    with open(os.path.join(ROOT, "profiles", f"prefill_mha_traffic_{wl}.json")) as f:
+        rec2 = json.load(f)
+    got2 = bench.load_traffic(wl, "prefill_mha")
+    if rec2["source_sha"] == bench.source_sha("prefill_mha"):
+        assert got2 == rec2["hbm_bytes_per_launch"]
+    else:
+        assert got2 is None
+    assert bench.source_sha("prefill_mha") != bench.source_sha("decode")
