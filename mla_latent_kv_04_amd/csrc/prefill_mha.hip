@@ -72,8 +72,18 @@ __global__ void __launch_bounds__(64 * NW, 1) mha_prefill_kernel(
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int g = lane >> 4, r16 = lane & 15;
-  const int h = blockIdx.y;
-  const int m0 = blockIdx.x * QB;
+  // Workgroup (query block, head), in dispatch order wid = x + gridDim.x y.
+  // Dispatch deals workgroup ids round-robin to the 8 XCDs; with n_h a
+  // multiple of 8 the query blocks of one head get ids 8 apart, so they run
+  // on one XCD at about the same time and read the head's k^C and v^C tiles
+  // through its L2 (otherwise each XCD streams them from HBM).
+  int h = blockIdx.y, qb = blockIdx.x;
+  if (n_h % 8 == 0) {
+    const int wid = blockIdx.x + gridDim.x * blockIdx.y, rest = wid >> 3;
+    qb = rest % gridDim.x;
+    h = (rest / gridDim.x) * 8 + (wid & 7);
+  }
+  const int m0 = qb * QB;
   const int mw = m0 + 32 * wave;                 // this wave's first query row (chunk index)
   const int shift = L - q_len + 1;               // row m sees keys j < shift + m (and j < L)
   const int m_top = min(m0 + QB, q_len) - 1;
