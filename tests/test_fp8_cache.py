@@ -149,6 +149,37 @@ def test_fp8_decode_matches_attention_over_the_dequantised_rows(case):
             1.0, float(np.abs(lref[fin]).max()))
 
 
+@pytest.mark.parametrize("wl,kw,S", [(F2, dict(B=2, ctx=[300, 256]), 1),
+                                     (F3, dict(B=2, ctx=[300, 256]), 1),
+                                     (F3, dict(B=2, ctx=[300, 256]), 0)],
+                         ids=["16-heads", "128-heads", "128-heads-planned"])
+def test_fp8_out_of_range_block_ids_are_skipped(wl, kw, S):
+    """A block id outside [0, num_blocks) drops that block's keys (their rows
+    are zeroed with unit scales in LDS and masked)."""
+    import torch
+    prob = small(wl, **kw)
+    say(f"fp8 bad block id {wl} S={S}")
+    dp = pipeline.upload(prob, num_splits=S, cache="fp8")
+    pipeline.append(dp)
+    from mla_latent_kv_04_amd import _binding as mla
+    mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE)
+    table = dp.block_table.clone()
+    table[0, 1] = 10 ** 6                 # keys 64..127 of sequence 0 vanish
+    table[1, 3] = -5                      # keys 192..255 of sequence 1 vanish
+    dp.block_table = table
+    pipeline.decode(dp)
+    torch.cuda.synchronize()
+    host, q_lat = _host_cache(dp), to_np(dp.q_lat)
+    o_lat = to_np(dp.o_lat)
+    for b, gone in ((0, range(64, 128)), (1, range(192, 256))):
+        L = int(prob.seq_lens[b])
+        keep = np.array([j for j in range(L) if j not in gone])
+        codes, scales = _cache_rows(dp, host, b, L)
+        deq = orc.dequantize_rows(codes[keep], scales[keep], D_C)
+        ref, _ = orc.latent_attention(q_lat[b:b + 1], deq, [len(keep)], softmax_scale(), D_C)
+        assert rel_err(o_lat[b:b + 1], ref) <= TOL["bf16"], b
+
+
 @pytest.mark.timeout(600)
 def test_fp8_step_full_size_lite_every_output():
     """The V2-Lite decode workload (B=64, 16 heads, L=4096) with the FP8

@@ -399,11 +399,18 @@ def test_empty_and_short_sequences():
     assert (o_lat[:2].cpu().numpy() == 0).all()
 
 
-def test_out_of_range_block_ids_are_skipped():
+@pytest.mark.parametrize("wl,kw,S", [(F2, dict(B=2, ctx=256), None),
+                                     (F3, dict(B=2, ctx=[300, 256]), 1),
+                                     (F3, dict(B=2, ctx=[300, 256]), 0)],
+                         ids=["16-heads", "128-heads", "128-heads-planned"])
+def test_out_of_range_block_ids_are_skipped(wl, kw, S):
+    """A block id outside [0, num_blocks) drops that block's keys: the rest of
+    the row is attended as if they were absent (16 heads: decode.hip; 128
+    heads: the two-role kernel, uniform and planned schedules)."""
     import torch
-    prob = small(F2, B=2, ctx=256)
-    say("bad block id")
-    dp = run_step(prob)
+    prob = small(wl, **kw)
+    say(f"bad block id {wl} S={S}")
+    dp = run_step(prob, num_splits=S)
     ref_full = to_np(dp.o_lat)
     table = dp.block_table.clone()
     table[0, 1] = 10 ** 6                 # keys 64..127 of sequence 0 vanish
@@ -413,7 +420,7 @@ def test_out_of_range_block_ids_are_skipped():
     torch.cuda.synchronize()
     q_lat, cache = to_np(dp.q_lat), to_np(dp.kv_cache)
     for b, gone in ((0, range(64, 128)), (1, range(192, 256))):
-        keep = [j for j in range(256) if j not in gone]
+        keep = [j for j in range(int(prob.seq_lens[b])) if j not in gone]
         rows = np.stack([cache[prob.block_table[b, j // BLOCK], j % BLOCK] for j in keep])
         ol, _ = orc.latent_attention(q_lat[b:b + 1], rows, [len(keep)], softmax_scale(), D_C)
         assert rel_err(to_np(dp.o_lat)[b:b + 1], ol) <= 1e-2
