@@ -119,9 +119,11 @@ def _oracle_on_gpu_rows(dp, host, q_lat_all, b, rows=None):
     (F2, dict(B=2, ctx=[700, 2000], n_h=32), 3),
     (F3, dict(B=3, ctx=[1500, 64, 333]), 2),
     (F5, dict(ctx=700, q_len=40, n_h=16), 1),
+    (F5, dict(ctx=700, q_len=70), 1),
     (F2, dict(B=5, ctx=[3000, 10, 4096, 700, 1]), 0),
     (F3, dict(B=4, ctx=[2000, 1, 900, 64]), 0),
-], ids=["lite-S1", "lite-S4", "h32-S3", "h128-S2", "chunk-q40", "lite-planned", "h128-planned"])
+], ids=["lite-S1", "lite-S4", "h32-S3", "h128-S2", "chunk-q40", "chunk-q70-h128", "lite-planned",
+        "h128-planned"])
 def test_fp8_decode_matches_attention_over_the_dequantised_rows(case):
     import torch
     wl, kw, S = case
