@@ -392,6 +392,33 @@ int o_chunk(int T, int N, int K) {
   return ((K + S - 1) / S + PK - 1) / PK * PK;
 }
 
+// bf16 W^O: K slice length and X-row tile.  The weight stream is the bound
+// and a slice's workgroups all start together, so the split fills one round
+// of the chip's workgroup slots rather than several: 256 with 128-row tiles
+// (one workgroup per CU, each weight tile staged once per slice) or 512 with
+// 64-row tiles (two per CU, each weight tile staged twice).  128-row tiles are
+// taken when T > 64 and they fill at least 3/4 of their round; the partials
+// cap is as above.  V2's decode shape (T = 128, 5120 x 16384): 40 tiles x 6
+// slices, 57 us against 77 us for 80 tiles x 8 slices (640 workgroups, a
+// quarter of them in a second round).
+int o_chunk_bf16(int T, int N, int K, int& tt) {
+  constexpr long CUS = 256;
+  const long cap = std::max(1L, std::min((long)K / 512, (long)K / (16L * std::max(T, 1))));
+  const long ntile = (N + PN - 1) / PN;
+  const long tiles128 = ntile * ((T + 127) / 128), tiles64 = ntile * ((T + 63) / 64);
+  const long s128 = std::max(1L, std::min(CUS / tiles128, cap));
+  const long s64 = std::max(1L, std::min(2 * CUS / tiles64, cap));
+  long S;
+  if (T > 64 && tiles128 * s128 * 4 >= CUS * 3) {
+    tt = 128;
+    S = s128;
+  } else {
+    tt = 64;
+    S = s64;
+  }
+  return (int)(((K + S - 1) / S + PK - 1) / PK * PK);
+}
+
 // eq. 8: u = W^O [o_1; ...; o_nh] for T rows of the heads' fp32 outputs.  In
 // bf16 the outputs are rounded to bf16 once (workspace) to feed the MFMA;
 // K = n_h 128 is split over workgroups into fp32 partials when the output
@@ -400,7 +427,8 @@ template <class E>
 hipError_t o_proj(const float* out, const void* w_o, int T, int n_h, int d_model, void* u,
                   void* workspace, hipStream_t stream) {
   const int K = n_h * D_H;
-  const int kc = o_chunk(T, d_model, K);
+  int tt = 0;
+  const int kc = E::bytes == 2 ? o_chunk_bf16(T, d_model, K, tt) : o_chunk(T, d_model, K);
   const int S = (K + kc - 1) / kc;
   char* ws = static_cast<char*>(workspace);
   const long xb = E::bytes == 2 ? ((long)T * K * 2 + 255) / 256 * 256 : 0;
@@ -420,7 +448,7 @@ hipError_t o_proj(const float* out, const void* w_o, int T, int n_h, int d_model
     }
     proj_bf16<OUT_PARTIAL>(XSrc{xh, K, nullptr, 0}, T, K, kc,
                            ProjOut{static_cast<const uint16_t*>(w_o), d_model, part, d_model, 0, 0},
-                           ProjOut{nullptr, 0, nullptr, 0, 0, 0}, stream);
+                           ProjOut{nullptr, 0, nullptr, 0, 0, 0}, stream, tt);
   } else {
     if (S == 1) {
       gemm_f32<E>(out, w_o, T, d_model, K, K, true, nullptr, d_model, 0, u, stream);
@@ -438,7 +466,8 @@ hipError_t o_proj(const float* out, const void* w_o, int T, int n_h, int d_model
 long o_proj_workspace(int T, int n_h, int d_model, int dtype) {
   const int K = n_h * D_H;
   const long xb = dtype == 1 ? ((long)T * K * 2 + 255) / 256 * 256 : 0;
-  const int kc = o_chunk(T, d_model, K);
+  int tt = 0;
+  const int kc = dtype == 1 ? o_chunk_bf16(T, d_model, K, tt) : o_chunk(T, d_model, K);
   const int S = (K + kc - 1) / kc;
   return xb + (S > 1 ? (long)S * T * d_model * 4 : 0);
 }

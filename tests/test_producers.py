@@ -151,10 +151,13 @@ def test_direct_query_producer_matches_oracle(dtype, d_model, n_h):
             assert rel_err(g, ref) <= 1e-5
 
 
-@pytest.mark.parametrize("dtype,T,n_h,d_model", [("bf16", 128, 128, 5120), ("f32", 33, 2, 192)])
+@pytest.mark.parametrize("dtype,T,n_h,d_model", [("bf16", 128, 128, 5120), ("bf16", 130, 128, 5120),
+                                                 ("bf16", 37, 128, 5120), ("f32", 33, 2, 192)])
 def test_o_proj_matches_oracle(dtype, T, n_h, d_model):
     """eq. 8's u = W^O [o_1; ...; o_nh]: at the V2 shape (128 tokens, 128 heads,
-    hidden 5120: K split over workgroups) and a small fp32 case."""
+    hidden 5120: K split over workgroups, 128-row tiles, a shorter last
+    slice), with a ragged second row tile (130), with 64-row tiles (37), and a
+    small fp32 case."""
     import torch
     from mla_latent_kv_04_amd import _binding as mla
     rng = np.random.default_rng(T + n_h)
