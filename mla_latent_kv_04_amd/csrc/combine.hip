@@ -7,8 +7,10 @@
 //
 // One workgroup per (row, pair of heads); a thread owns 4 of the 512 dims.
 // This pass is bandwidth bound: it reads S x 2 KB per head once.  The parts
-// are read MERGE_BATCH at a time, all loads of a batch in flight together,
-// and summed in part order.
+// are read MERGE_BATCH at a time, their lse and data loads all in flight
+// together, and summed in part order against a running maximum (what is
+// summed so far is rescaled when a batch raises it), so a row of up to
+// MERGE_BATCH parts costs one round trip to memory.
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -16,34 +18,45 @@ namespace mla {
 
 namespace {
 
-constexpr int MERGE_BATCH = 8;
+constexpr int MERGE_BATCH = 16;
 
-// sum_k w_k x_k and sum_k w_k over parts k = 0..count-1 at p(k) (element
-// offsets of the lse entries; the output row is D_C floats per lse entry),
-// w_k = exp(lse_k - mx), a part with lse -inf weighing nothing.
+// Over parts k = 0..count-1 at p(k) (element offsets of the lse entries; the
+// output row is D_C floats per lse entry): m = max_k lse_k, z = sum_k w_k and
+// o = sum_k w_k x_k with w_k = exp(lse_k - m); a part with lse -inf weighs
+// nothing, and m stays -inf (z = 0) when every part does.
 template <class PartAt>
 __device__ __forceinline__ void merge_parts(const float* __restrict__ o_part,
                                             const float* __restrict__ lse_part, int count,
-                                            PartAt part_at, float mx, int d4, float4& o, float& z) {
+                                            PartAt part_at, int d4, float4& o, float& z, float& m) {
   for (int k0 = 0; k0 < count; k0 += MERGE_BATCH) {
-    float w[MERGE_BATCH];
+    float l[MERGE_BATCH];
     float4 x[MERGE_BATCH];
 #pragma unroll
     for (int u = 0; u < MERGE_BATCH; ++u) {
-      w[u] = 0.0f;
+      l[u] = -INFINITY;
       x[u] = float4{0, 0, 0, 0};
       if (k0 + u < count) {
         const long pr = part_at(k0 + u);
-        const float l = lse_part[pr];
-        w[u] = l == -INFINITY ? 0.0f : __expf(l - mx);
+        l[u] = lse_part[pr];
         x[u] = reinterpret_cast<const float4*>(o_part + pr * D_C)[d4];
       }
     }
+    float mb = m;
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u) mb = fmaxf(mb, l[u]);
+    if (mb == -INFINITY) continue;
+    if (mb > m) {
+      const float f = m == -INFINITY ? 0.0f : __expf(m - mb);
+      z *= f;
+      o.x *= f; o.y *= f; o.z *= f; o.w *= f;
+      m = mb;
+    }
 #pragma unroll
     for (int u = 0; u < MERGE_BATCH; ++u) {
-      if (w[u] == 0.0f) continue;
-      z += w[u];
-      o.x += w[u] * x[u].x; o.y += w[u] * x[u].y; o.z += w[u] * x[u].z; o.w += w[u] * x[u].w;
+      if (l[u] == -INFINITY) continue;
+      const float w = __expf(l[u] - m);
+      z += w;
+      o.x += w * x[u].x; o.y += w * x[u].y; o.z += w * x[u].z; o.w += w * x[u].w;
     }
   }
 }
@@ -60,13 +73,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   // partial (b, s, m, head) lives at ((b * S + s) * q_len + m) * n_h + head
   const long step = (long)q_len * n_h;    // distance between consecutive splits
   const long p0 = ((long)b * S * q_len + m) * n_h + head;
-  float mx = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, lse_part[p0 + s * step]);
   float4 o = {0, 0, 0, 0};
-  float z = 0.0f;
-  if (mx != -INFINITY)
-    merge_parts(o_part, lse_part, S, [&](int s) { return p0 + s * step; }, mx, d4, o, z);
+  float z = 0.0f, mx = -INFINITY;
+  merge_parts(o_part, lse_part, S, [&](int s) { return p0 + s * step; }, d4, o, z, mx);
   const float inv = z > 0.0f ? 1.0f / z : 0.0f;
   reinterpret_cast<float4*>(o_lat + ((long)row * n_h + head) * D_C)[d4] =
       float4{o.x * inv, o.y * inv, o.z * inv, o.w * inv};
@@ -83,14 +92,10 @@ __global__ void __launch_bounds__(256) combine_planned_kernel(
   if (head >= n_h) return;
   const int row = split[blockIdx.x * 3], first = split[blockIdx.x * 3 + 1];
   const int count = split[blockIdx.x * 3 + 2];
-  float mx = -INFINITY;
-#pragma unroll 8
-  for (int k = 0; k < count; ++k) mx = fmaxf(mx, lse_part[(long)(first + k) * n_h + head]);
   float4 o = {0, 0, 0, 0};
-  float z = 0.0f;
-  if (mx != -INFINITY)
-    merge_parts(o_part, lse_part, count,
-                [&](int k) { return (long)(first + k) * n_h + head; }, mx, d4, o, z);
+  float z = 0.0f, mx = -INFINITY;
+  merge_parts(o_part, lse_part, count, [&](int k) { return (long)(first + k) * n_h + head; }, d4,
+              o, z, mx);
   const float inv = z > 0.0f ? 1.0f / z : 0.0f;
   reinterpret_cast<float4*>(o_lat + ((long)row * n_h + head) * D_C)[d4] =
       float4{o.x * inv, o.y * inv, o.z * inv, o.w * inv};
