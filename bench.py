@@ -10,8 +10,10 @@ lengths uniform in [1024, 8192], paged blocks of 64 tokens, bf16).
 Prints ONE JSON line.  ``value`` is query tokens per second of the whole step.
 ``roofline`` covers the dominant kernel (the paged attention kernel): its
 algorithmic bytes (or FLOPs) per launch divided by its mean launch time,
-measured with HIP events on the stream it runs on.  ``cpu_baseline`` times the
-float64 CPU oracle on a bounded sample of the same workload.
+measured with HIP events on the stream it runs on, recorded by the kernel's
+own dispatch (the library's mla_time_attention) over a second pass of as many
+steps: the timed steps themselves carry no timing packets.  ``cpu_baseline`` times the float64
+CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -34,7 +36,7 @@ PRODUCER_EPS = 1e-6           # RMSNorm epsilon of the latent and query norms
 # used while these are unchanged
 DECODE_SOURCES = ["mla_latent_kv_04_amd/csrc/decode.hip", "mla_latent_kv_04_amd/csrc/decode_h64.hip",
                   "mla_latent_kv_04_amd/csrc/decode_h64_fp8.hip", "mla_latent_kv_04_amd/csrc/decode_h64_common.h",
-                  "mla_latent_kv_04_amd/csrc/decode_fp8.hip",
+                  "mla_latent_kv_04_amd/csrc/decode_fp8.hip", "mla_latent_kv_04_amd/csrc/attention_launch.h",
                   "mla_latent_kv_04_amd/csrc/mla_common.h", "mla_latent_kv_04_amd/csrc/mla_api.cpp"]
 
 
@@ -304,7 +306,9 @@ def main():
 
     pf_ws = pipeline.prefill_workspace(dp) if non_absorbed else None
 
-    def one_step(ev=None):
+    def one_step(ev=None, timer=None):
+        """One step.  ev: events recorded around the step's parts (indices
+        below); timer: a KernelTimer armed for the attention kernel."""
         if non_absorbed:
             mla.mla_kv_append(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r, dp.new_seq,
                               dp.new_pos, ROPE_BASE)
@@ -334,6 +338,8 @@ def main():
         mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE)
         if ev is not None:
             ev[0].record(stream)
+        if timer is not None:
+            timer.arm()
         attend()
         if ev is not None:
             ev[1].record(stream)
@@ -405,17 +411,24 @@ def main():
             def record(self, _stream):
                 self.rec.calls.append(("__event__", self.k))
 
+            def arm(self):
+                self.rec.calls.append(("__arm__", None))
+
         with mla.recording() as rec:
-            one_step(tuple(_Mark(rec, k) for k in range(7)))
+            one_step(tuple(_Mark(rec, k) for k in range(7)), _Mark(rec, None))
         step_calls = rec.calls
         lib = mla.load()
         checked_step = one_step
 
-        def one_step(ev=None):
+        def one_step(ev=None, timer=None):
             for name, a in step_calls:
                 if name == "__event__":
                     if ev is not None:
                         ev[a].record(stream)
+                    continue
+                if name == "__arm__":
+                    if timer is not None:
+                        lib.mla_time_attention(timer.start, timer.stop)
                     continue
                 st = getattr(lib, name)(*a)
                 if st != 0:
@@ -432,23 +445,43 @@ def main():
             one_step()
         settle += 20
         torch.cuda.synchronize()
-    n_ev = 7 if hw is not None else 2
-    events = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(n_ev))
-              for _ in range(args.steps)]
-    step_ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
-               for _ in range(args.steps)]
+    # The timed steps carry no timing packets: an event recorded between two
+    # kernels leaves the GPU idle for ~5 us, also when the kernel's own
+    # dispatch records it.  The attention kernel is timed in a second pass of
+    # as many identical steps, by its own dispatch (the library launches it
+    # with a start / stop event pair, mla_time_attention); the non-absorbed
+    # call is several kernels and is timed with events recorded around it.
+    dispatch_timed = not non_absorbed
+
+    def new_events(n):
+        return tuple(torch.cuda.Event(enable_timing=True) for _ in range(n))
+
+    def new_timers(n):
+        return [mla.KernelTimer() for _ in range(n)] if dispatch_timed else [None] * n
+
+    timers = new_timers(args.steps)
+    events = [new_events(2) if non_absorbed else None for _ in range(args.steps)]
+    region = new_events(2)
     log(f"[bench] {settle} settle steps; timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record(stream)
     for i in range(args.steps):
-        step_ev[i][0].record(stream)
-        one_step(events[i])
-        step_ev[i][1].record(stream)
+        one_step()
+    region[1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dec_times = [e[0].elapsed_time(e[1]) for e in events]
-    timing = {"launch": args.launch, "warmup_steps": args.warmup, "settle_steps": settle}
+    step_gpu_us = region[0].elapsed_time(region[1]) * 1e3 / args.steps
+    for i in range(args.steps):
+        one_step(events[i], timers[i])
+    torch.cuda.synchronize()
+    dec_times = ([t.elapsed_ms() for t in timers] if dispatch_timed
+                 else [e[0].elapsed_time(e[1]) for e in events])
+    timing = {"launch": args.launch, "warmup_steps": args.warmup, "settle_steps": settle,
+              "attention_timing": (("the kernel's own dispatch events (mla_time_attention)"
+                                    if dispatch_timed else "events around the call")
+                                   + f", over a second pass of {args.steps} steps")}
     if args.launch == "graph":
         # Eager launches from Python cost tens of microseconds each, more than a
         # small step's kernels: the GPU then idles between them.  A graph of one
@@ -466,15 +499,15 @@ def main():
             g_att.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        region[0].record(stream)
         for i in range(args.steps):
-            step_ev[i][0].record(stream)
             g_step.replay()
-            step_ev[i][1].record(stream)
+        region[1].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         ms_per_step = (t1 - t0) * 1e3 / args.steps
-        att_ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2))
-                  for _ in range(args.steps)]
+        step_gpu_us = region[0].elapsed_time(region[1]) * 1e3 / args.steps
+        att_ev = [new_events(2) for _ in range(args.steps)]
         for i in range(args.steps):
             att_ev[i][0].record(stream)
             g_att.replay()
@@ -484,19 +517,30 @@ def main():
         del g_step, g_att
     dec_ms = float(np.mean(dec_times))
     timing["attention_us"] = spread(dec_times)
-    timing["step_us"] = spread([e[0].elapsed_time(e[1]) for e in step_ev])
+    timing["step_gpu_us"] = round(step_gpu_us, 2)   # GPU time of the timed steps / steps
     if args.cold_steps > 0:
         # each step after a 1 GiB write: the cache rows, queries and weights
         # come from HBM, not from the L2 / last-level cache
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        cold = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(n_ev))
-                for _ in range(args.cold_steps)]
+        cold_t = new_timers(args.cold_steps)
+        cold_e = [new_events(2) if non_absorbed else None for _ in range(args.cold_steps)]
         for i in range(args.cold_steps):
             flush.fill_(float(i))
-            one_step(cold[i])
+            one_step(cold_e[i], cold_t[i])
         torch.cuda.synchronize()
-        timing["attention_cold_us"] = spread([e[0].elapsed_time(e[1]) for e in cold])
+        timing["attention_cold_us"] = spread(
+            [t.elapsed_ms() for t in cold_t] if dispatch_timed
+            else [e[0].elapsed_time(e[1]) for e in cold_e])
         del flush
+    prod_events = None
+    if hw is not None:
+        # the producers and W^O, timed with events around each (a separate
+        # pass of as many steps, so that these events stay out of the timed
+        # steps)
+        prod_events = [new_events(7) for _ in range(args.steps)]
+        for i in range(args.steps):
+            one_step(prod_events[i])
+        torch.cuda.synchronize()
     tokens = prob.T
     value = tokens / (ms_per_step * 1e-3)
 
@@ -520,9 +564,9 @@ def main():
 
     producers = None
     if hw is not None:
-        kv_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
-        q_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in events]))
-        o_ms = (float(np.mean([e[5].elapsed_time(e[6]) for e in events]))
+        kv_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in prod_events]))
+        q_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in prod_events]))
+        o_ms = (float(np.mean([e[5].elapsed_time(e[6]) for e in prod_events]))
                 if splits == 0 else None)
         o_by = (prob.T * wl.n_h * 128 * 4 + d_model * wl.n_h * 128 * (2 if wl.dtype == "bf16" else 4)
                 + prob.T * d_model * (2 if wl.dtype == "bf16" else 4))

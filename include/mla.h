@@ -54,7 +54,8 @@
  *   [0, num_blocks) contributes no keys and receives no rows) instead of
  *   faulting.  No C++ exception crosses this interface.  All entry points are
  *   thread-safe: the library holds no mutable global state, apart from the
- *   per-device scratch array of mla_decode_paged_noalloc (see there).
+ *   per-device scratch array of mla_decode_paged_noalloc and the per-thread
+ *   timing events of mla_time_attention (see there).
  */
 #ifndef MLA_LATENT_KV_MLA_H
 #define MLA_LATENT_KV_MLA_H
@@ -65,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 3
+#define MLA_ABI_VERSION 4
 
 #define MLA_D_C 512
 #define MLA_D_R 64
@@ -514,6 +515,26 @@ int32_t mla_decode_paged_noalloc(const void* q_lat, const void* kv_cache, int32_
                                  int32_t max_blocks, const int32_t* seq_lens, int32_t B,
                                  int32_t q_len, int32_t n_h, int32_t dtype, float softmax_scale,
                                  int32_t num_splits, float* o_lat, float* lse, void* stream);
+
+/*
+ * mla_time_attention - kernel timing, for benchmarks and profilers that time
+ * the attention kernel inside a running pipeline.  The events (hipEvent_t
+ * handles created by the caller on the current device, timing enabled) are
+ * armed for the calling host thread: the next attention kernel that thread
+ * launches (the paged-attention kernel of mla_decode_paged,
+ * mla_decode_paged_planned, mla_decode_paged_fp8,
+ * mla_decode_paged_planned_fp8 or mla_decode_paged_noalloc) is dispatched
+ * with them (hipExtLaunchKernel): `start` records the time that kernel starts
+ * and `stop` the time it ends, so hipEventElapsedTime(start, stop) is its
+ * duration.  Unlike hipEventRecord around the call, no timing packet is queued
+ * between the kernels, so the timed pipeline runs as it does untimed.  The
+ * launch disarms; a call that launches no attention kernel (no work, or an
+ * argument error) leaves the events armed.  Arming again replaces the armed
+ * pair; mla_time_attention(NULL, NULL) disarms.  Either event may be NULL.
+ * Returns MLA_OK; the events are not checked here (a launch with an invalid
+ * event returns MLA_ERR_HIP).  Other host threads are unaffected.
+ */
+int32_t mla_time_attention(void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,8 @@ _EXPORTS = ("mla_status_string", "mla_abi_version", "mla_rope_theta", "mla_kv_ap
             "mla_q_produce_workspace", "mla_q_produce", "mla_q_produce_direct",
             "mla_o_proj_workspace", "mla_o_proj",
             "mla_prefill_mha_workspace", "mla_prefill_mha", "mla_kv_append_fp8",
-            "mla_decode_paged_fp8", "mla_decode_paged_planned_fp8", "mla_decode_paged_noalloc")
+            "mla_decode_paged_fp8", "mla_decode_paged_planned_fp8", "mla_decode_paged_noalloc",
+            "mla_time_attention")
 
 
 class MLAError(RuntimeError):
@@ -110,6 +111,7 @@ def load() -> ctypes.CDLL:
     sig = {
         "mla_status_string": (ctypes.c_char_p, [_I]),
         "mla_abi_version": (_I, []),
+        "mla_time_attention": (_I, [_P, _P]),
         "mla_rope_theta": (_I, [_D, _D, _D, _D, _D, _P]),
         "mla_kv_append": (_I, [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I, _F, _P, _P]),
         "mla_absorb_q": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P]),
@@ -736,3 +738,67 @@ def mla_decode_paged_planned_fp8(q_lat, kv_cache, kv_scale, block_table, B, q_le
         _dev(lse_part, "lse_part", f32), n_parts, _dev(o_lat, "o_lat", f32), _dev(lse, "lse", f32),
         _stream(stream))
     _check("mla_decode_paged_planned_fp8", st)
+
+
+# ---------------------------------------------------------------------------
+# Kernel timing
+# ---------------------------------------------------------------------------
+
+def mla_time_attention(start_event, stop_event):
+    """Arm this thread's next attention launch with two HIP event handles
+    (raw hipEvent_t values, or None): the dispatch records its own start and
+    end in them (see mla.h)."""
+    _check("mla_time_attention", load().mla_time_attention(start_event, stop_event))
+
+
+_hip_rt: Optional[ctypes.CDLL] = None
+
+
+def _hip():
+    """The HIP runtime the library runs on (already loaded with it)."""
+    global _hip_rt
+    if _hip_rt is None:
+        load()
+        rt = ctypes.CDLL("libamdhip64.so.7")
+        rt.hipEventCreate.argtypes = [ctypes.POINTER(_P)]
+        rt.hipEventDestroy.argtypes = [_P]
+        rt.hipEventSynchronize.argtypes = [_P]
+        rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(_F), _P, _P]
+        for fn in (rt.hipEventCreate, rt.hipEventDestroy, rt.hipEventSynchronize,
+                   rt.hipEventElapsedTime):
+            fn.restype = ctypes.c_int
+        _hip_rt = rt
+    return _hip_rt
+
+
+class KernelTimer:
+    """A start / stop pair of HIP events (timing enabled, current device) for
+    mla_time_attention: ``arm()`` before the attention call, ``elapsed_ms()``
+    once the stream has passed the kernel."""
+
+    def __init__(self):
+        rt = _hip()
+        self.start, self.stop = _P(), _P()
+        for ev in (self.start, self.stop):
+            if rt.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+
+    def arm(self):
+        mla_time_attention(self.start, self.stop)
+
+    def elapsed_ms(self) -> float:
+        rt = _hip()
+        if rt.hipEventSynchronize(self.stop) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = _F()
+        st = rt.hipEventElapsedTime(ctypes.byref(ms), self.start, self.stop)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st}): events not recorded")
+        return float(ms.value)
+
+    def close(self):
+        if _hip_rt is not None:
+            for ev in (self.start, self.stop):
+                if ev.value:
+                    _hip_rt.hipEventDestroy(ev)
+                    ev.value = None

@@ -23,6 +23,7 @@
 // key that sets the maximum gets a weight above 1 that is rounded to bf16
 // like every other weight, instead of exactly 1.
 #include "mla_common.h"
+#include "attention_launch.h"
 #include "mla_internal.h"
 
 namespace mla {
@@ -345,11 +346,10 @@ hipError_t launch(const void* q_lat, const void* cache, int num_blocks, const in
   if (n_items == 0) return hipSuccess;
   dim3 grid((unsigned)n_items, n_h / C::HG), block(C::THREADS);
   using T = typename E::storage;
-  hipLaunchKernelGGL((decode_kernel<E, C>), grid, block, 0, stream, (const T*)q_lat,
-                     (const T*)cache, num_blocks, table, max_blocks, seq_lens, q_len, n_h,
-                     B * q_len, n_parts, scale * LOG2E, S, (const int4*)work, o_lat, lse, o_part,
-                     lse_part);
-  return hipGetLastError();
+  return launch_attention(decode_kernel<E, C>, grid, block, stream, (const T*)q_lat,
+                          (const T*)cache, num_blocks, table, max_blocks, seq_lens, q_len, n_h,
+                          B * q_len, n_parts, scale * LOG2E, S, (const int4*)work, o_lat, lse,
+                          o_part, lse_part);
 }
 
 #define MLA_DECODE_ARGS q_lat, cache, num_blocks, table, max_blocks, seq_lens, B, q_len, n_h, \

@@ -25,6 +25,7 @@
 // compute unit fit in its 160 KB of LDS (16 and 32 heads; with 64 heads per
 // workgroup the registers allow one).
 #include "mla_common.h"
+#include "attention_launch.h"
 #include "mla_internal.h"
 
 namespace mla {
@@ -330,11 +331,10 @@ hipError_t launch8(const void* q_lat, const void* cache, const float* kv_scale, 
   const long n_items = work != nullptr ? (long)n_work : (long)B * q_len * S;
   if (n_items == 0) return hipSuccess;
   dim3 grid((unsigned)n_items, n_h / C::HG), block(C::THREADS);
-  hipLaunchKernelGGL((decode_fp8_kernel<C>), grid, block, 0, stream, (const uint16_t*)q_lat,
-                     (const uint8_t*)cache, kv_scale, num_blocks, table, max_blocks, seq_lens,
-                     q_len, n_h, B * q_len, n_parts, scale * LOG2E, S, (const int4*)work, o_lat,
-                     lse, o_part, lse_part);
-  return hipGetLastError();
+  return launch_attention(decode_fp8_kernel<C>, grid, block, stream, (const uint16_t*)q_lat,
+                          (const uint8_t*)cache, kv_scale, num_blocks, table, max_blocks,
+                          seq_lens, q_len, n_h, B * q_len, n_parts, scale * LOG2E, S,
+                          (const int4*)work, o_lat, lse, o_part, lse_part);
 }
 
 }  // namespace

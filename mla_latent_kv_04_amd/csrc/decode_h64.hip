@@ -57,6 +57,7 @@
 // with 64-token tiles, decode_h64_fp8.hip; the helpers both use are in
 // decode_h64_common.h.)
 #include "mla_common.h"
+#include "attention_launch.h"
 #include "mla_internal.h"
 #include "decode_h64_common.h"
 
@@ -529,11 +530,10 @@ hipError_t launch_decode_h64(const void* q_lat, const void* cache, int num_block
   const int ngroups = n_h / HG;
   const long wgs = (n_units + 7) / 8 * 8 * ngroups;
   if (wgs == 0 || n_items == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_h64_kernel, dim3((unsigned)wgs), dim3(NTHREADS), 0, stream,
-                     (const uint16_t*)q_lat, cache, num_blocks, table,
-                     max_blocks, seq_lens, q_len, n_h, (int)n_items, B * q_len, n_parts, scale * LOG2E, S,
-                     (const int4*)work, lists, n_lists, o_lat, lse, o_part, lse_part);
-  return hipGetLastError();
+  return launch_attention(decode_h64_kernel, dim3((unsigned)wgs), dim3(NTHREADS), stream,
+                          (const uint16_t*)q_lat, cache, num_blocks, table, max_blocks, seq_lens,
+                          q_len, n_h, (int)n_items, B * q_len, n_parts, scale * LOG2E, S,
+                          (const int4*)work, lists, n_lists, o_lat, lse, o_part, lse_part);
 }
 
 }  // namespace mla

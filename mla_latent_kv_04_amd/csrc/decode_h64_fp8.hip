@@ -41,6 +41,7 @@
 //            max by more than 2^8 (log2), the new max is agreed, P(a) and the
 //            normaliser redone and the accumulators rescaled (one more barrier).
 #include "mla_common.h"
+#include "attention_launch.h"
 #include "mla_internal.h"
 #include "decode_h64_common.h"
 
@@ -533,12 +534,11 @@ hipError_t launch_decode_h64_fp8(const void* q_lat, const void* cache, const flo
   const int ngroups = n_h / HG;
   const long wgs = (n_units + 7) / 8 * 8 * ngroups;
   if (wgs == 0 || n_items == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_h64_fp8_kernel, dim3((unsigned)wgs), dim3(NTHREADS), 0, stream,
-                     (const uint16_t*)q_lat, (const uint8_t*)cache, kv_scale, num_blocks, table,
-                     max_blocks, seq_lens, q_len, n_h, (int)n_items, B * q_len, n_parts,
-                     scale * LOG2E, S, (const int4*)work, lists, n_lists, o_lat, lse, o_part,
-                     lse_part);
-  return hipGetLastError();
+  return launch_attention(decode_h64_fp8_kernel, dim3((unsigned)wgs), dim3(NTHREADS), stream,
+                          (const uint16_t*)q_lat, (const uint8_t*)cache, kv_scale, num_blocks,
+                          table, max_blocks, seq_lens, q_len, n_h, (int)n_items, B * q_len,
+                          n_parts, scale * LOG2E, S, (const int4*)work, lists, n_lists, o_lat,
+                          lse, o_part, lse_part);
 }
 
 }  // namespace mla

@@ -22,7 +22,16 @@ bool decode_heads_ok(int32_t n_h) { return n_h == 16 || n_h == 32 || (n_h > 0 &&
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Events armed by mla_time_attention, per host thread.
+thread_local mla::KernelEvents armed_events{nullptr, nullptr};
+
 }  // namespace
+
+mla::KernelEvents mla::take_attention_events() {
+  const KernelEvents ev = armed_events;
+  armed_events = KernelEvents{nullptr, nullptr};
+  return ev;
+}
 
 extern "C" {
 
@@ -40,6 +49,11 @@ const char* mla_status_string(int32_t status) {
 }
 
 int32_t mla_abi_version(void) { return MLA_ABI_VERSION; }
+
+int32_t mla_time_attention(void* start_event, void* stop_event) {
+  armed_events = mla::KernelEvents{(hipEvent_t)start_event, (hipEvent_t)stop_event};
+  return MLA_OK;
+}
 
 int32_t mla_rope_theta(double base, double scale, double alpha, double beta, double orig_ctx,
                        double* theta) {

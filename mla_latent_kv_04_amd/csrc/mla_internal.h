@@ -8,6 +8,13 @@
 
 namespace mla {
 
+// Kernel timing (mla_time_attention).  The events this thread armed, taken
+// (and disarmed) by its next attention launch; both null when none are armed.
+struct KernelEvents {
+  hipEvent_t start, stop;
+};
+KernelEvents take_attention_events();
+
 // RoPE pair frequencies theta_k (radians per position) of the 64-wide
 // decoupled key, k = 0..31, passed by value to the kernels that rotate.
 struct RopeFreq {

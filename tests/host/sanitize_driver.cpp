@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "mla.h"
+#include "mla_internal.h"
 
 extern int g_launches;
 
@@ -143,6 +144,14 @@ void entry_points() {
   for (int s = -1; s < 9; ++s)
     if (mla_status_string(s) == nullptr) ++failures;
   if (mla_abi_version() != MLA_ABI_VERSION) ++failures;
+  // arming stores the handles for this thread; the next launch takes them
+  int ev0 = 0, ev1 = 0;
+  EXPECT(mla_time_attention(&ev0, &ev1), MLA_OK);
+  const mla::KernelEvents armed = mla::take_attention_events();
+  if (armed.start != (hipEvent_t)&ev0 || armed.stop != (hipEvent_t)&ev1) ++failures;
+  const mla::KernelEvents after = mla::take_attention_events();
+  if (after.start != nullptr || after.stop != nullptr) ++failures;
+  EXPECT(mla_time_attention(nullptr, nullptr), MLA_OK);
   if (g_launches - before < 16) {
     std::printf("only %d launches reached the stand-ins\n", g_launches - before);
     ++failures;
