@@ -319,7 +319,9 @@ def main():
                 ev[1].record(stream)
             return
         if hw is None:
-            pipeline.append(dp)
+            # the step's new rows and its latent queries (one launch for the
+            # native cache)
+            pipeline.append_absorb(dp)
         else:
             if ev is not None:
                 ev[2].record(stream)
@@ -335,7 +337,7 @@ def main():
                 mla.mla_q_produce_direct(hw["h"], hw["w_qc"], hw["w_qr"], dp.q_nope, dp.q_rope)
             if ev is not None:
                 ev[4].record(stream)
-        mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE)
+            mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE)
         if ev is not None:
             ev[0].record(stream)
         if timer is not None:

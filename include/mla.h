@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 4
+#define MLA_ABI_VERSION 5
 
 #define MLA_D_C 512
 #define MLA_D_R 64
@@ -161,6 +161,28 @@ int32_t mla_kv_append(void* kv_cache, int32_t dtype, int32_t num_blocks, int32_t
 int32_t mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
                      const int32_t* q_pos, int32_t T, int32_t n_h, int32_t dtype,
                      float rope_base, const double* rope_theta, void* q_lat, void* stream);
+
+/*
+ * mla_append_absorb_q - the two calls that open a decode step, in one launch:
+ * mla_kv_append (the step's n new rows into the cache) and mla_absorb_q (the
+ * step's T latent queries), with the same dtype and RoPE frequencies.  The
+ * arguments, layouts, results and skipped rows are those of the two calls;
+ * each part is checked as its call checks it, and only when it is not empty
+ * (n > 0, T > 0): an error in either returns its status with nothing
+ * enqueued.  The two parts run concurrently, so the cache must not overlap
+ * q_lat, q_nope, q_rope or w_uk.  Between the two operations of a step
+ * (DeepSeek-V2 MLA blog, adg.csdn.net, part 2 §2.2.2: the new token's latent
+ * row and rotated key are cached, and its query is absorbed into latent
+ * space) there is no data dependence; one launch saves a kernel boundary.
+ * bf16 runs as one kernel; fp32 as the two launches.
+ */
+int32_t mla_append_absorb_q(void* kv_cache, int32_t num_blocks, int32_t block_size,
+                            const int32_t* block_table, int32_t num_seqs, int32_t max_blocks,
+                            const void* c_kv, const void* k_rope, const int32_t* seq_idx,
+                            const int32_t* pos, int32_t n, const void* q_nope,
+                            const void* q_rope, const void* w_uk, const int32_t* q_pos,
+                            int32_t T, int32_t n_h, int32_t dtype, float rope_base,
+                            const double* rope_theta, void* q_lat, void* stream);
 
 /*
  * mla_decode_paged - attention of latent queries over the paged cache.

@@ -26,7 +26,7 @@ _EXPORTS = ("mla_status_string", "mla_abi_version", "mla_rope_theta", "mla_kv_ap
             "mla_o_proj_workspace", "mla_o_proj",
             "mla_prefill_mha_workspace", "mla_prefill_mha", "mla_kv_append_fp8",
             "mla_decode_paged_fp8", "mla_decode_paged_planned_fp8", "mla_decode_paged_noalloc",
-            "mla_time_attention")
+            "mla_time_attention", "mla_append_absorb_q")
 
 
 class MLAError(RuntimeError):
@@ -112,6 +112,8 @@ def load() -> ctypes.CDLL:
         "mla_status_string": (ctypes.c_char_p, [_I]),
         "mla_abi_version": (_I, []),
         "mla_time_attention": (_I, [_P, _P]),
+        "mla_append_absorb_q": (_I, [_P, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P,
+                                     _I, _I, _I, _F, _P, _P, _P]),
         "mla_rope_theta": (_I, [_D, _D, _D, _D, _D, _P]),
         "mla_kv_append": (_I, [_P, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _I, _F, _P, _P]),
         "mla_absorb_q": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _P, _P, _P]),
@@ -280,6 +282,43 @@ def mla_absorb_q(q_nope, q_rope, w_uk, q_pos, q_lat, rope_base=10000.0, stream=N
                              _dev(q_pos, "q_pos", torch.int32), T, n_h, dt, float(rope_base),
                              _ptr(th), _dev(q_lat, "q_lat"), _stream(stream))
     _check("mla_absorb_q", st)
+
+
+def mla_append_absorb_q(kv_cache, block_table, c_kv, k_rope, seq_idx, pos, q_nope, q_rope, w_uk,
+                        q_pos, q_lat, rope_base=10000.0, stream=None, rope_theta=None):
+    """mla_kv_append and mla_absorb_q of one step in one launch (see mla.h)."""
+    torch = _torch()
+    dt = _dtype_code(q_nope)
+    if kv_cache.dtype != q_nope.dtype:
+        raise TypeError("kv_cache dtype differs from q_nope")
+    n = int(c_kv.shape[0])
+    for name, t in (("c_kv", c_kv), ("k_rope", k_rope)):
+        if t.dtype != kv_cache.dtype:
+            raise TypeError(f"{name} dtype differs from the cache")
+    if tuple(c_kv.shape) != (n, D_C) or tuple(k_rope.shape) != (n, D_R):
+        raise ValueError("c_kv must be [n, 512] and k_rope [n, 64]")
+    if tuple(seq_idx.shape) != (n,) or tuple(pos.shape) != (n,):
+        raise ValueError("seq_idx and pos must be [n]")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != ROW:
+        raise ValueError("kv_cache must be [num_blocks, 64, 576]")
+    T, n_h = int(q_nope.shape[0]), int(q_nope.shape[1])
+    if tuple(q_nope.shape) != (T, n_h, D_H) or tuple(q_rope.shape) != (T, n_h, D_R):
+        raise ValueError("q_nope must be [T, n_h, 128] and q_rope [T, n_h, 64]")
+    if tuple(w_uk.shape) != (n_h, D_H, D_C) or tuple(q_lat.shape) != (T, n_h, ROW):
+        raise ValueError("w_uk must be [n_h, 128, 512] and q_lat [T, n_h, 576]")
+    for name, t in (("q_rope", q_rope), ("w_uk", w_uk), ("q_lat", q_lat)):
+        if t.dtype != q_nope.dtype:
+            raise TypeError(f"{name} dtype differs from q_nope")
+    th = _theta(rope_theta)
+    st = load().mla_append_absorb_q(
+        _dev(kv_cache, "kv_cache"), int(kv_cache.shape[0]), int(kv_cache.shape[1]),
+        _dev(block_table, "block_table", torch.int32), int(block_table.shape[0]),
+        int(block_table.shape[1]), _dev(c_kv, "c_kv"), _dev(k_rope, "k_rope"),
+        _dev(seq_idx, "seq_idx", torch.int32), _dev(pos, "pos", torch.int32), n,
+        _dev(q_nope, "q_nope"), _dev(q_rope, "q_rope"), _dev(w_uk, "w_uk"),
+        _dev(q_pos, "q_pos", torch.int32), T, n_h, dt, float(rope_base), _ptr(th),
+        _dev(q_lat, "q_lat"), _stream(stream))
+    _check("mla_append_absorb_q", st)
 
 
 def mla_decode_paged(q_lat, kv_cache, block_table, seq_lens, q_len, softmax_scale, num_splits=1,

@@ -31,6 +31,7 @@
 // float64, 4 of the 32 pairs per column tile.
 #include <cmath>
 
+#include "append_row.h"
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -200,15 +201,15 @@ __global__ void __launch_bounds__(256) absorb_q_f32_kernel(
 // Tile c + PF is loaded into registers while tile c is multiplied; the LDS
 // holds two tiles.
 template <int CPW, int PF>
-__global__ void __launch_bounds__(256) absorb_q_bf16_kernel(
-    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
-    const uint16_t* __restrict__ w_uk, const int* __restrict__ q_pos, int T, int n_h, RopeRev rev,
-    uint16_t* __restrict__ q_lat) {
+__device__ __forceinline__ void absorb_bf16_group(
+    int h, int gy, int z, const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ w_uk, const int* __restrict__ q_pos, int T, int n_h,
+    const RopeRev& rev, uint16_t* __restrict__ q_lat) {
   constexpr int S = AbsorbLds<BF16>::stride;
   constexpr int NG = (D_C / CCH) / CPW;   // column groups per head
   __shared__ __attribute__((aligned(16))) char lds[2][D_H * S];
   constexpr int TBW = TCH / 64;           // 16-row blocks per wave
-  const int h = blockIdx.x, gy = blockIdx.y, t0 = blockIdx.z * TCH;
+  const int t0 = z * TCH;
   const int tid = threadIdx.x;
   const int lane = lane_id(), wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
 
@@ -318,6 +319,57 @@ __global__ void __launch_bounds__(256) absorb_q_bf16_kernel(
   }
 }
 
+template <int CPW, int PF>
+__global__ void __launch_bounds__(256) absorb_q_bf16_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ w_uk, const int* __restrict__ q_pos, int T, int n_h, RopeRev rev,
+    uint16_t* __restrict__ q_lat) {
+  absorb_bf16_group<CPW, PF>(blockIdx.x, blockIdx.y, blockIdx.z, q_nope, q_rope, w_uk, q_pos, T,
+                             n_h, rev, q_lat);
+}
+
+// The step's append and absorb in one launch (bf16): workgroups 0 .. n_app-1
+// append four cache rows each (one per wave), the others are the absorb's
+// (h, gy, z) workgroups in the order of the plain launch's grid.  The two
+// parts share no data; one launch saves a kernel boundary, and the append's
+// short dependent loads run beside the absorb.
+template <int CPW, int PF>
+__global__ void __launch_bounds__(256) append_absorb_bf16_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_rope,
+    const uint16_t* __restrict__ w_uk, const int* __restrict__ q_pos, int T, int n_h, RopeRev rev,
+    uint16_t* __restrict__ q_lat, int n_app, uint16_t* __restrict__ cache, int num_blocks,
+    const int* __restrict__ table, int num_seqs, int max_blocks, const uint16_t* __restrict__ c_kv,
+    const uint16_t* __restrict__ k_rope, const int* __restrict__ seq_idx,
+    const int* __restrict__ pos, int n, RopeFreq rf) {
+  const int wg = blockIdx.x;
+  if (wg < n_app) {
+    const int r = wg * 4 + (threadIdx.x >> 6);
+    if (r < n)
+      append_row<BF16>(cache, num_blocks, table, num_seqs, max_blocks, c_kv, k_rope, seq_idx, pos,
+                       r, threadIdx.x & 63, rf);
+    return;
+  }
+  constexpr int NG = (D_C / CCH) / CPW;
+  const int a = wg - n_app;
+  absorb_bf16_group<CPW, PF>(a % n_h, (a / n_h) % NG, a / (n_h * NG), q_nope, q_rope, w_uk, q_pos,
+                             T, n_h, rev, q_lat);
+}
+
+// Tiles per workgroup by the number of (head, 128-row) units: measured on
+// 16 x 64, 128 x 128 and 128 x 2048 (heads x rows), one tile per workgroup
+// keeps a few heads spread over the chip; four, with three tiles in flight,
+// suits long prefill chunks.  Returns CPW (PF follows from it).
+int absorb_cpw(int n_h, int nz) {
+  const int units = n_h * nz;
+  return units >= 1024 ? 4 : units >= 64 ? 2 : 1;
+}
+
+RopeRev rope_rev(const RopeFreq& rf) {
+  RopeRev rev;
+  for (int k = 0; k < D_R / 2; ++k) rev.r[k] = rf.theta[k] / 6.283185307179586;
+  return rev;
+}
+
 }  // namespace
 
 hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
@@ -330,27 +382,69 @@ hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w
                        n_h, rf, (float*)q_lat);
     return hipGetLastError();
   }
-  RopeRev rev;
-  for (int k = 0; k < D_R / 2; ++k)
-    rev.r[k] = rf.theta[k] / 6.283185307179586;
+  const RopeRev rev = rope_rev(rf);
   auto* q = (const uint16_t*)q_nope;
   auto* r = (const uint16_t*)q_rope;
   auto* w = (const uint16_t*)w_uk;
   auto* o = (uint16_t*)q_lat;
-  // tiles per workgroup by the number of (head, 128-row) units: measured on
-  // 16 x 64, 128 x 128 and 128 x 2048 (heads x rows), one tile per
-  // workgroup keeps a few heads spread over the chip; four, with three tiles
-  // in flight, suits long prefill chunks
-  const int units = n_h * nz;
-  if (units >= 1024)
+  const int cpw = absorb_cpw(n_h, nz);
+  if (cpw == 4)
     hipLaunchKernelGGL((absorb_q_bf16_kernel<4, 3>), dim3(n_h, 2, nz), dim3(256), 0, stream, q, r,
                        w, q_pos, T, n_h, rev, o);
-  else if (units >= 64)
+  else if (cpw == 2)
     hipLaunchKernelGGL((absorb_q_bf16_kernel<2, 2>), dim3(n_h, 4, nz), dim3(256), 0, stream, q, r,
                        w, q_pos, T, n_h, rev, o);
   else
     hipLaunchKernelGGL((absorb_q_bf16_kernel<1, 2>), dim3(n_h, 8, nz), dim3(256), 0, stream, q, r,
                        w, q_pos, T, n_h, rev, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_absorb(void* cache, int dtype, int num_blocks, const int* table,
+                                int num_seqs, int max_blocks, const void* c_kv,
+                                const void* k_rope, const int* seq_idx, const int* pos, int n,
+                                const void* q_nope, const void* q_rope, const void* w_uk,
+                                const int* q_pos, int T, int n_h, const RopeFreq& rf,
+                                void* q_lat, hipStream_t stream) {
+  if (dtype != 1) {
+    // fp32: the two launches (the reference-precision path is not fused)
+    if (n > 0) {
+      const hipError_t e = launch_kv_append(cache, dtype, num_blocks, table, num_seqs,
+                                            max_blocks, c_kv, k_rope, seq_idx, pos, n, rf,
+                                            stream);
+      if (e != hipSuccess) return e;
+    }
+    return T > 0 ? launch_absorb_q(q_nope, q_rope, w_uk, q_pos, T, n_h, dtype, rf, q_lat, stream)
+                 : hipSuccess;
+  }
+  const int nz = (T + TCH - 1) / TCH;
+  // append workgroups first (a multiple of 8, so that the absorb's
+  // workgroups keep their XCDs), so that their dependent loads start first
+  const int n_app = (n + 31) / 32 * 8;
+  const int cpw = absorb_cpw(n_h, nz);
+  const long n_abs = (long)n_h * (D_C / CCH / cpw) * nz;
+  const long grid = n_app + n_abs;
+  if (grid == 0) return hipSuccess;
+  const RopeRev rev = rope_rev(rf);
+  auto* q = (const uint16_t*)q_nope;
+  auto* r = (const uint16_t*)q_rope;
+  auto* w = (const uint16_t*)w_uk;
+  auto* o = (uint16_t*)q_lat;
+  auto* kc = (uint16_t*)cache;
+  auto* cs = (const uint16_t*)c_kv;
+  auto* kr = (const uint16_t*)k_rope;
+  if (cpw == 4)
+    hipLaunchKernelGGL((append_absorb_bf16_kernel<4, 3>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, q, r, w, q_pos, T, n_h, rev, o, n_app, kc, num_blocks, table,
+                       num_seqs, max_blocks, cs, kr, seq_idx, pos, n, rf);
+  else if (cpw == 2)
+    hipLaunchKernelGGL((append_absorb_bf16_kernel<2, 2>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, q, r, w, q_pos, T, n_h, rev, o, n_app, kc, num_blocks, table,
+                       num_seqs, max_blocks, cs, kr, seq_idx, pos, n, rf);
+  else
+    hipLaunchKernelGGL((append_absorb_bf16_kernel<1, 2>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, q, r, w, q_pos, T, n_h, rev, o, n_app, kc, num_blocks, table,
+                       num_seqs, max_blocks, cs, kr, seq_idx, pos, n, rf);
   return hipGetLastError();
 }
 

@@ -107,6 +107,35 @@ int32_t mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk,
                                          (hipStream_t)stream));
 }
 
+int32_t mla_append_absorb_q(void* kv_cache, int32_t num_blocks, int32_t block_size,
+                            const int32_t* block_table, int32_t num_seqs, int32_t max_blocks,
+                            const void* c_kv, const void* k_rope, const int32_t* seq_idx,
+                            const int32_t* pos, int32_t n, const void* q_nope,
+                            const void* q_rope, const void* w_uk, const int32_t* q_pos,
+                            int32_t T, int32_t n_h, int32_t dtype, float rope_base,
+                            const double* rope_theta, void* q_lat, void* stream) {
+  if (!dtype_ok(dtype)) return MLA_ERR_DTYPE;
+  mla::RopeFreq rf;
+  if (n < 0 || T < 0 || !mla::rope_freq(rope_base, rope_theta, rf)) return MLA_ERR_SHAPE;
+  if (n > 0) {  // the checks of mla_kv_append
+    if (num_blocks < 1 || num_seqs < 1 || max_blocks < 1 || block_size != MLA_BLOCK)
+      return MLA_ERR_SHAPE;
+    if (!kv_cache || !block_table || !c_kv || !k_rope || !seq_idx || !pos) return MLA_ERR_NULL;
+    if (!aligned16(kv_cache) || !aligned16(c_kv) || !aligned4(k_rope)) return MLA_ERR_ALIGN;
+  }
+  if (T > 0) {  // the checks of mla_absorb_q
+    if (n_h < 16 || n_h % 16 != 0) return MLA_ERR_SHAPE;
+    if (!q_nope || !q_rope || !w_uk || !q_pos || !q_lat) return MLA_ERR_NULL;
+    if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat) || !aligned4(q_rope))
+      return MLA_ERR_ALIGN;
+  }
+  if (n == 0 && T == 0) return MLA_OK;
+  return hip_status(mla::launch_append_absorb(kv_cache, dtype, num_blocks, block_table, num_seqs,
+                                              max_blocks, c_kv, k_rope, seq_idx, pos, n, q_nope,
+                                              q_rope, w_uk, q_pos, T, n_h, rf, q_lat,
+                                              (hipStream_t)stream));
+}
+
 int32_t mla_decode_paged(const void* q_lat, const void* kv_cache, int32_t num_blocks,
                          int32_t block_size, const int32_t* block_table, int32_t max_blocks,
                          const int32_t* seq_lens, int32_t B, int32_t q_len, int32_t n_h,

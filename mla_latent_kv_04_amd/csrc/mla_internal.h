@@ -48,6 +48,15 @@ hipError_t launch_absorb_q(const void* q_nope, const void* q_rope, const void* w
                            const int* q_pos, int T, int n_h, int dtype, const RopeFreq& rf,
                            void* q_lat, hipStream_t stream);
 
+// launch_kv_append and launch_absorb_q of one step, in one launch for bf16
+// (absorb_q.hip); either part may be empty (n == 0 or T == 0).
+hipError_t launch_append_absorb(void* cache, int dtype, int num_blocks, const int* table,
+                                int num_seqs, int max_blocks, const void* c_kv,
+                                const void* k_rope, const int* seq_idx, const int* pos, int n,
+                                const void* q_nope, const void* q_rope, const void* w_uk,
+                                const int* q_pos, int T, int n_h, const RopeFreq& rf,
+                                void* q_lat, hipStream_t stream);
+
 // Paged attention.  Uniform splits when work == nullptr (S splits per row,
 // partials at row (b * S + s) * q_len + m when S > 1), else a work list of
 // n_work int4 {row, key_begin, key_end, slot}; n_parts bounds the slots (an

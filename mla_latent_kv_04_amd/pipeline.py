@@ -188,12 +188,25 @@ def append(dp: DeviceProblem, stream=None):
                           dp.new_pos, ROPE_BASE, stream=stream)
 
 
+def append_absorb(dp: DeviceProblem, stream=None):
+    """The step's new rows into the cache and its latent queries: one launch
+    (mla_append_absorb_q) for the native cache, the two calls for the FP8 one."""
+    if dp.kv_scale is not None:
+        append(dp, stream)
+        mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE,
+                         stream=stream)
+    else:
+        mla.mla_append_absorb_q(dp.kv_cache, dp.block_table, dp.new_c_kv, dp.new_k_r,
+                                dp.new_seq, dp.new_pos, dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos,
+                                dp.q_lat, ROPE_BASE, stream=stream)
+
+
 def step(dp: DeviceProblem, stream=None):
-    """One pass of the hot path: append -> absorb -> decode -> combine -> out-proj.
-    Under a balanced plan the combine runs inside the out-projection's loads
-    (dp.o_lat then holds only the rows the plan did not split)."""
-    append(dp, stream)
-    mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat, ROPE_BASE, stream=stream)
+    """One pass of the hot path: append + absorb -> decode -> combine ->
+    out-proj.  Under a balanced plan the combine runs inside the
+    out-projection's loads (dp.o_lat then holds only the rows the plan did not
+    split)."""
+    append_absorb(dp, stream)
     if dp.num_splits == 0:
         _attend_planned(dp, stream)
         mla.mla_out_proj_planned(dp.o_lat, dp.o_part, dp.lse_part, dp.split, dp.w_uv, dp.out,

@@ -29,6 +29,12 @@ hipError_t launch_absorb_q(const void*, const void*, const void*, const int*, in
                            const RopeFreq&, void*, hipStream_t) {
   return counted();
 }
+hipError_t launch_append_absorb(void*, int, int, const int*, int, int, const void*, const void*,
+                                const int*, const int*, int, const void*, const void*,
+                                const void*, const int*, int, int, const RopeFreq&, void*,
+                                hipStream_t) {
+  return counted();
+}
 hipError_t launch_decode(const void*, const void*, int, const int*, int, const int*, int, int, int,
                          int, float, int, const int*, int, const int*, int, float*, float*, float*,
                          float*, int, hipStream_t) {

@@ -109,6 +109,26 @@ void entry_points() {
          MLA_ERR_NULL);
   EXPECT(mla_absorb_q(F, F, F, FI, 4, 16, 1, 1e4, good, F, nullptr), MLA_OK);
   EXPECT(mla_absorb_q(F, F, F, FI, 4, 24, 1, 1e4, nullptr, F, nullptr), MLA_ERR_SHAPE);
+  EXPECT(mla_append_absorb_q(F, 4, 64, FI, 1, 4, F, F, FI, FI, 3, F, F, F, FI, 4, 16, 1, 1e4,
+                             nullptr, F, nullptr), MLA_OK);
+  EXPECT(mla_append_absorb_q(F, 4, 64, FI, 1, 4, F, F, FI, FI, 0, F, F, F, FI, 4, 16, 1, 1e4,
+                             good, F, nullptr), MLA_OK);
+  EXPECT(mla_append_absorb_q(nullptr, 4, 64, FI, 1, 4, F, F, FI, FI, 0, F, F, F, FI, 4, 16, 1,
+                             1e4, good, F, nullptr), MLA_OK);
+  EXPECT(mla_append_absorb_q(MIS, 4, 64, FI, 1, 4, F, F, FI, FI, 3, F, F, F, FI, 4, 16, 1, 1e4,
+                             good, F, nullptr), MLA_ERR_ALIGN);
+  EXPECT(mla_append_absorb_q(F, 4, 32, FI, 1, 4, F, F, FI, FI, 3, F, F, F, FI, 4, 16, 1, 1e4,
+                             good, F, nullptr), MLA_ERR_SHAPE);
+  EXPECT(mla_append_absorb_q(F, 4, 64, FI, 1, 4, F, F, FI, FI, 3, F, F, F, FI, 4, 24, 1, 1e4,
+                             good, F, nullptr), MLA_ERR_SHAPE);
+  EXPECT(mla_append_absorb_q(F, 4, 64, FI, 1, 4, F, F, FI, FI, 3, F, F, F, FI, 0, 24, 1, 1e4,
+                             good, F, nullptr), MLA_OK);
+  EXPECT(mla_append_absorb_q(F, 4, 64, FI, 1, 4, F, F, FI, FI, 3, nullptr, F, F, FI, 4, 16, 1,
+                             1e4, good, F, nullptr), MLA_ERR_NULL);
+  EXPECT(mla_append_absorb_q(F, 4, 64, FI, 1, 4, F, F, FI, FI, 3, F, F, F, FI, 4, 16, 7, 1e4,
+                             good, F, nullptr), MLA_ERR_DTYPE);
+  EXPECT(mla_append_absorb_q(F, 4, 64, FI, 1, 4, F, F, FI, FI, 3, F, F, F, FI, 4, 16, 1, 1e4,
+                             bad, F, nullptr), MLA_ERR_SHAPE);
   EXPECT(mla_decode_paged(F, F, 4, 64, FI, 4, FI, 2, 1, 128, 1, 0.07f, 3, FF, FF, FF, FF, nullptr),
          MLA_OK);
   EXPECT(mla_decode_paged(F, F, 4, 64, FI, 4, FI, 2, 1, 48, 1, 0.07f, 1, FF, FF, FF, FF, nullptr),

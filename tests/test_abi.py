@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 4
+    assert lib.mla_abi_version() == 5
     for s in range(7):
         assert len(B.status_string(s)) > 0
     assert "scratch" in B.status_string(6)
