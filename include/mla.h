@@ -329,14 +329,15 @@ int32_t mla_combine_planned(const float* o_part, const float* lse_part, const in
 
 /*
  * mla_out_proj_planned - mla_combine_planned followed by mla_out_proj, in one
- * pass for bf16 weights and T > 64: the split rows of a plan (split device
- * int32 [n_split, 3] from mla_plan_decode, rows distinct and increasing) are
- * merged from o_part / lse_part with the log-sum-exp rule of
- * mla_splitkv_combine as they are loaded, and their LSE is written to lse
- * (device fp32 [T, n_h], may be NULL); every other row is read from o_lat.
- * The merged rows of o_lat are scratch: after the call they hold either the
- * merged value (fp32 weights, and T <= 64, where the two steps run one after
- * the other so that both spread over the chip) or what they held before.
+ * launch for bf16 weights: the split rows of a plan (split device int32
+ * [n_split, 3] from mla_plan_decode, rows distinct and increasing) are merged
+ * from o_part / lse_part with the log-sum-exp rule of mla_splitkv_combine
+ * (as they are loaded for T > 64; into on-chip memory, a few rows per
+ * workgroup, for T <= 64), and their LSE is written to lse (device fp32
+ * [T, n_h], may be NULL); every other row is read from o_lat.  The merged
+ * rows of o_lat are scratch: after the call they hold either the merged value
+ * (fp32 weights, where the two steps run one after the other) or what they
+ * held before.
  * Other arguments, layouts and the bf16 hi + lo split of the operand as in
  * mla_out_proj.  0 <= n_split <= T; T == 0 is a no-op.
  */

@@ -20,6 +20,7 @@
 // the schedule cut into several key ranges has its partial outputs merged
 // with the log-sum-exp rule (each part weighted by exp(lse_k - LSE)) as the
 // row's o_lat operand is loaded, so the merged row never goes to memory.
+#include "merge_parts.h"
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -344,6 +345,83 @@ __global__ void __launch_bounds__(64) out_proj_small_kernel(const float* __restr
         float4{acc[0], acc[1], acc[2], acc[3]};
 }
 
+// Few rows under a split-KV plan (T <= SMALL_T, bf16 weights): merge and
+// project in one launch.  Workgroup (h, SMALL_ROWS-row block): its threads
+// first put the block's o_lat rows in LDS, one (row, 4 dims) each -- a split
+// row merged from its parts (merge_parts, as combine_planned_kernel does; its
+// LSE written to lse), any other row copied from o_lat -- then wave w
+// multiplies W^UV_h rows 16w .. 16w + 15 by them with the MFMA sequence of
+// out_proj_small_kernel (bf16 hi + lo).  The merged row takes the same values
+// as through memory, so the outputs equal merge-then-project bit for bit.
+constexpr int SMALL_ROWS = 4;
+constexpr int LAT_PITCH = D_C + 4;        // floats per LDS row (rows 4 banks apart)
+
+__global__ void __launch_bounds__(512) out_proj_small_planned_kernel(
+    const float* __restrict__ o_lat, const float* __restrict__ o_part,
+    const float* __restrict__ lse_part, const int* __restrict__ split, int n_split,
+    const uint16_t* __restrict__ w_uv, int T, int n_h, float* __restrict__ out,
+    float* __restrict__ lse) {
+  static_assert(SMALL_ROWS * (D_C / 4) == 512, "one (row, 4 dims) per thread");
+  __shared__ __attribute__((aligned(16))) float lat[SMALL_ROWS][LAT_PITCH];
+  __shared__ int entry[SMALL_ROWS];
+  const int h = blockIdx.x, t0 = blockIdx.y * SMALL_ROWS;
+  const int tid = threadIdx.x;
+  if (tid < SMALL_ROWS) entry[tid] = -1;
+  __syncthreads();
+  // split-table entries of the block's rows (rows are distinct)
+  for (int j = tid; j < n_split; j += 512) {
+    const int r = split[3 * j];
+    if (r >= t0 && r < t0 + SMALL_ROWS) entry[r - t0] = j;
+  }
+  __syncthreads();
+  {
+    const int i = tid >> 7, d4 = tid & 127;
+    const int t = t0 + i;
+    float4 v = {0, 0, 0, 0};
+    if (t < T) {
+      const int j = entry[i];
+      if (j >= 0) {
+        const int first = split[3 * j + 1], count = split[3 * j + 2];
+        float4 o = {0, 0, 0, 0};
+        float z = 0.0f, mx = -INFINITY;
+        merge_parts(o_part, lse_part, count, [&](int k) { return (long)(first + k) * n_h + h; },
+                    d4, o, z, mx);
+        const float inv = z > 0.0f ? 1.0f / z : 0.0f;
+        v = float4{o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+        if (lse != nullptr && d4 == 0)
+          lse[(long)t * n_h + h] = z > 0.0f ? mx + __logf(z) : -INFINITY;
+      } else {
+        v = reinterpret_cast<const float4*>(o_lat + ((long)t * n_h + h) * D_C)[d4];
+      }
+    }
+    *reinterpret_cast<float4*>(&lat[i][4 * d4]) = v;
+  }
+  __syncthreads();
+  const int lane = lane_id(), wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int d0 = 16 * wave;
+  const uint16_t* wrow = w_uv + ((long)h * D_H + d0 + r16) * D_C + 8 * g;
+  BF16::frag wf[D_C / 32];
+#pragma unroll
+  for (int ks = 0; ks < D_C / 32; ++ks) wf[ks] = BF16::load8(wrow + ks * 32);
+  const bool row_ok = r16 < SMALL_ROWS;     // B rows past the block are zero
+  f32x4_t acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < D_C / 32; ++ks) {
+    const float* lp = &lat[row_ok ? r16 : 0][ks * 32 + 8 * g];
+    const float4 a = row_ok ? reinterpret_cast<const float4*>(lp)[0] : float4{0, 0, 0, 0};
+    const float4 b = row_ok ? reinterpret_cast<const float4*>(lp)[1] : float4{0, 0, 0, 0};
+    BF16::frag lf[2];
+    LatFrag<BF16>::split(a, b, lf);
+    BF16::mma(acc, wf[ks], lf[0]);
+    BF16::mma(acc, wf[ks], lf[1]);
+  }
+  // lane holds row t0 + r16 and outputs d0 + 4g .. d0 + 4g + 3
+  const int t = t0 + r16;
+  if (row_ok && t < T)
+    *reinterpret_cast<float4*>(out + ((long)t * n_h + h) * D_H + d0 + 4 * g) =
+        float4{acc[0], acc[1], acc[2], acc[3]};
+}
+
 template <class E>
 __global__ void __launch_bounds__(256) out_proj_kernel(const float* __restrict__ o_lat,
                                                        const typename E::storage* __restrict__ w_uv,
@@ -411,9 +489,21 @@ hipError_t launch_out_proj(const float* o_lat, const void* w_uv, int T, int n_h,
 hipError_t launch_out_proj_planned(float* o_lat, const float* o_part, const float* lse_part,
                                    const int* split, int n_split, const void* w_uv, int T, int n_h,
                                    int dtype, float* out, float* lse, hipStream_t stream) {
+  const long small_wgs = (long)n_h * ((T + SMALL_ROWS - 1) / SMALL_ROWS);
+  if (dtype == 1 && n_split > 0 && T <= SMALL_T && small_wgs >= 256) {
+    // few rows, enough (head, row block) pairs to fill the chip: merge and
+    // project in one launch.  With fewer (a handful of rows cut into many
+    // parts, as at 128K) the merge pass below spreads the parts over more
+    // workgroups: 9.9 against 15.5 us for 4 rows x 128 heads in ~64 parts.
+    hipLaunchKernelGGL(out_proj_small_planned_kernel,
+                       dim3(n_h, (T + SMALL_ROWS - 1) / SMALL_ROWS), dim3(512), 0, stream, o_lat,
+                       o_part, lse_part, split, n_split, (const uint16_t*)w_uv, T, n_h, out, lse);
+    return hipGetLastError();
+  }
   if (dtype != 1 || n_split == 0 || T <= SMALL_T) {
-    // fp32 weights, or few rows: merge into o_lat (a pass over all split rows
-    // at once), then the plain projection
+    // fp32 weights, no split row, or few rows on too few workgroups: merge
+    // into o_lat (a pass over all split rows at once), then the plain
+    // projection
     if (n_split > 0) {
       const hipError_t st =
           launch_combine_planned(o_part, lse_part, split, n_split, n_h, o_lat, lse, stream);

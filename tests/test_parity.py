@@ -311,6 +311,52 @@ def test_out_proj_planned_merges_split_rows(T, n_h, dtype, frac):
     np.testing.assert_allclose(got_l[fin], lref[fin], rtol=1e-6, atol=1e-5)
 
 
+# (T, n_h): one launch when the (head, 4-row block) pairs reach 256 (64 x 16,
+# ragged 61 x 16 and 33 x 64), the merge pass then the projection below that
+# (4 x 128, 17 x 32)
+FEW_ROWS = [(64, 16), (61, 16), (33, 64), (4, 128), (17, 32)]
+
+
+@pytest.mark.parametrize("T,n_h", FEW_ROWS, ids=[f"T{c[0]}-h{c[1]}" for c in FEW_ROWS])
+def test_few_row_planned_projection_equals_merge_then_project(T, n_h):
+    """For few rows (bf16 weights) the planned projection merges and projects
+    in one launch when that fills the chip; either way its outputs and LSE
+    equal mla_combine_planned followed by mla_out_proj bit for bit (the same
+    merge and the same MFMA sequence)."""
+    import torch
+    from mla_latent_kv_04_amd import _binding as mla
+    rng = np.random.default_rng(31)
+    rows = np.sort(rng.choice(T, size=max(1, T // 2), replace=False)).astype(np.int32)
+    counts = rng.integers(2, 40, size=len(rows)).astype(np.int32)   # up to three batches of parts
+    first = (np.cumsum(counts) - counts).astype(np.int32)
+    n_parts = int(counts.sum())
+    o_part = rng.standard_normal((n_parts, n_h, D_C)).astype(np.float32)
+    lse_part = (rng.standard_normal((n_parts, n_h)) * 4).astype(np.float32)
+    lse_part[rng.random((n_parts, n_h)) < 0.15] = -np.inf
+    lse_part[first[0]:first[0] + counts[0], 1] = -np.inf          # a row whose parts are all empty
+    o_part[np.isneginf(lse_part)] = 0.0
+    o_lat = rng.standard_normal((T, n_h, D_C)).astype(np.float32)
+    w = round_to_bf16((rng.standard_normal((n_h, 128, D_C)) / math.sqrt(D_C)).astype(np.float32))
+    split = torch.from_numpy(np.stack([rows, first, counts], axis=1).astype(np.int32)).cuda()
+    op, lp = torch.from_numpy(o_part).cuda(), torch.from_numpy(lse_part).cuda()
+    wt = torch.from_numpy(w).to(torch.bfloat16).cuda()
+    say(f"few-row planned projection T={T} n_h={n_h}: one launch")
+    lat1 = torch.from_numpy(o_lat).cuda()
+    out1 = torch.full((T, n_h, 128), float("nan"), device="cuda")
+    lse1 = torch.full((T, n_h), 7.0, device="cuda")
+    mla.mla_out_proj_planned(lat1, op, lp, split, wt, out1, lse1)
+    say(f"few-row planned projection T={T} n_h={n_h}: merge, then project")
+    lat2 = torch.from_numpy(o_lat).cuda()
+    out2 = torch.full((T, n_h, 128), float("nan"), device="cuda")
+    lse2 = torch.full((T, n_h), 7.0, device="cuda")
+    mla.mla_combine_planned(op, lp, split, n_h, lat2, lse2)
+    mla.mla_out_proj(lat2, wt, out2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out1.cpu().numpy().view(np.int32), out2.cpu().numpy().view(np.int32))
+    assert np.array_equal(lse1.cpu().numpy().view(np.int32), lse2.cpu().numpy().view(np.int32))
+    assert torch.isfinite(out1).all()
+
+
 # Balanced schedules with few slots, so that lists hold many items and rows
 # are cut into many parts: (workload, batch, context range, q_len, n_h, slots).
 DENSE_PLANS = [(F3, 9, (1, 1500), 1, 128, 5), (F3, 3, (1500, 3000), 1, 64, 5),
