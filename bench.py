@@ -480,6 +480,9 @@ def main():
     torch.cuda.synchronize()
     dec_times = ([t.elapsed_ms() for t in timers] if dispatch_timed
                  else [e[0].elapsed_time(e[1]) for e in events])
+    for t in timers:
+        if t is not None:
+            t.close()
     timing = {"launch": args.launch, "warmup_steps": args.warmup, "settle_steps": settle,
               "attention_timing": (("the kernel's own dispatch events (mla_time_attention)"
                                     if dispatch_timed else "events around the call")
@@ -533,6 +536,9 @@ def main():
         timing["attention_cold_us"] = spread(
             [t.elapsed_ms() for t in cold_t] if dispatch_timed
             else [e[0].elapsed_time(e[1]) for e in cold_e])
+        for t in cold_t:
+            if t is not None:
+                t.close()
         del flush
     prod_events = None
     if hw is not None:

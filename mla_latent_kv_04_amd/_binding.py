@@ -813,7 +813,9 @@ def _hip():
 class KernelTimer:
     """A start / stop pair of HIP events (timing enabled, current device) for
     mla_time_attention: ``arm()`` before the attention call, ``elapsed_ms()``
-    once the stream has passed the kernel."""
+    once the stream has passed the kernel, ``close()`` to release the events
+    (not left to garbage collection, which may run after the runtime has shut
+    down)."""
 
     def __init__(self):
         rt = _hip()
