@@ -92,3 +92,35 @@ def test_call_without_launch_leaves_the_events_armed():
     finally:
         timer.close()
         mla.mla_time_attention(None, None)
+
+
+def test_planned_and_noalloc_launches_record_their_events():
+    """The balanced-plan entry point and the allocation-free one launch their
+    attention kernel through the same armed path."""
+    import torch
+    prob = small("v2_bf16_B4_L128k_splitkv", B=2, ctx=[1900, 700])
+    dp = pipeline.upload(prob, num_splits=0)
+    pipeline.append(dp)
+    mla.mla_absorb_q(dp.q_nope, dp.q_rope, dp.w_uk, dp.q_pos, dp.q_lat)
+    torch.cuda.synchronize()
+    timer = mla.KernelTimer()
+    try:
+        say("timing: planned launch")
+        timer.arm()
+        pipeline._attend_planned(dp)
+        ms = timer.elapsed_ms()
+        assert math.isfinite(ms) and 0.0 < ms < 1000.0, ms
+        say("timing: allocation-free launch")
+        rows = dp.B * dp.q_len
+        o_lat = torch.empty((rows, dp.n_h, D_C), device="cuda")
+        lse = torch.empty((rows, dp.n_h), device="cuda")
+        timer.arm()
+        mla.mla_decode_paged_noalloc(dp.q_lat, dp.kv_cache, dp.block_table, dp.seq_lens,
+                                     dp.q_len, softmax_scale(), 3, o_lat, lse)
+        ms = timer.elapsed_ms()
+        torch.cuda.synchronize()
+        assert math.isfinite(ms) and 0.0 < ms < 1000.0, ms
+        assert torch.isfinite(o_lat).all()
+    finally:
+        timer.close()
+        mla.mla_time_attention(None, None)
